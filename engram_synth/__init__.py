@@ -288,11 +288,24 @@ def decode_tokens(cfg: Config, step: int) -> np.ndarray:
     return zipf_tokens(rng, cfg.n_seqs, cfg.map_len)
 
 
-def hidden_bf16(cfg: Config, layer: int, T: int, batch: int = 0) -> np.ndarray:
-    """mHC hidden at layer entry, N(0,1) rounded to BF16: uint16[T][hc][H]."""
-    rng = np.random.default_rng([cfg.root, STREAM_HIDDEN, layer, batch])
-    x = rng.standard_normal((T, cfg.hc, cfg.H), dtype=np.float32)
-    return bf16_bits_from_f32(x)
+HIDDEN_CHUNK = 4096
+
+
+def hidden_bf16(cfg: Config, layer: int, T: int, batch: int = 0, first: int = 0) -> np.ndarray:
+    """mHC hidden at layer entry, N(0,1) rounded to BF16: uint16[T][hc][H]
+    for token rows [first, first+T). Rows are drawn in chunks of HIDDEN_CHUNK
+    tokens, each from its own stream, so any row range can be regenerated
+    alone and chunks can be generated in parallel."""
+    out = np.empty((T, cfg.hc, cfg.H), dtype=np.uint16)
+    if T == 0:
+        return out
+    for c in range(first // HIDDEN_CHUNK, (first + T - 1) // HIDDEN_CHUNK + 1):
+        rng = np.random.default_rng([cfg.root, STREAM_HIDDEN, layer, batch, c])
+        x = rng.standard_normal((HIDDEN_CHUNK, cfg.hc, cfg.H), dtype=np.float32)
+        a = max(first, c * HIDDEN_CHUNK)
+        b = min(first + T, (c + 1) * HIDDEN_CHUNK)
+        out[a - first:b - first] = bf16_bits_from_f32(x[a - c * HIDDEN_CHUNK:b - c * HIDDEN_CHUNK])
+    return out
 
 
 def wkv_bf16(cfg: Config, layer: int) -> np.ndarray:

@@ -1,0 +1,332 @@
+"""Python binding of libengram, the MI355X (gfx950) Engram forward path.
+
+Argument marshalling only: every function checks the tensors' dtype, device
+and contiguity, then calls the C entry point of the same name with raw
+pointers and torch's current HIP stream. All computation happens in the HIP
+kernels; there is no CPU fallback. Importing this package fails if
+libengram.so has not been built (python -m gram_hashed_embedding_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "EngramError", "HashParams", "lib",
+    "engram_check_params", "engram_history_reset", "engram_history_fork",
+    "engram_history_append", "engram_hash", "engram_gather_decode", "engram_project",
+    "engram_gate", "engram_forward_workspace", "engram_forward", "engram_gen_table",
+    "DEAD_TOKEN", "DEAD_IDX", "BUCKETS", "MEM", "STAGE_EVENTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+
+DEAD_TOKEN = 0xFFFFFFFF
+DEAD_IDX = 0xFFFFFFFF
+BUCKETS = 24
+MEM = 6144
+STAGE_EVENTS = 5
+
+ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EHIP, ENGRAM_EUNSUPPORTED = 0, -1, -2, -3
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: {_status(status)}: {detail}")
+        self.status = status
+
+
+class HashParams(ctypes.Structure):
+    """Mirror of engram_hash_params (one layer's hash tables)."""
+    _fields_ = [
+        ("mult", (ctypes.c_uint64 * 4) * 24),
+        ("prime", ctypes.c_uint32 * 24),
+        ("offset", ctypes.c_uint64 * 24),
+        ("n_rows", ctypes.c_uint64),
+        ("vocab_c", ctypes.c_uint32),
+        ("pad_cid", ctypes.c_uint32),
+    ]
+
+    @classmethod
+    def make(cls, mult, prime, offset, n_rows: int, vocab_c: int, pad_cid: int) -> "HashParams":
+        p = cls()
+        m = np.asarray(mult, dtype=np.uint64).reshape(24, 4)
+        for j in range(24):
+            for k in range(4):
+                p.mult[j][k] = int(m[j, k])
+            p.prime[j] = int(np.asarray(prime)[j])
+            p.offset[j] = int(np.asarray(offset)[j])
+        p.n_rows, p.vocab_c, p.pad_cid = int(n_rows), int(vocab_c), int(pad_cid)
+        return p
+
+    @classmethod
+    def from_any(cls, obj) -> "HashParams":
+        """Accept a HashParams or any object with mult/prime/offset/n_rows/vocab_c/pad_cid."""
+        if isinstance(obj, cls):
+            return obj
+        return cls.make(obj.mult, obj.prime, obj.offset, obj.n_rows, obj.vocab_c, obj.pad_cid)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m gram_hashed_embedding_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, U32, U64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float,
+                                      ctypes.c_size_t)
+    sigs = {
+        "engram_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "engram_last_error": ([], ctypes.c_char_p),
+        "engram_abi_version": ([], ctypes.c_int),
+        "engram_check_params": ([P, P, U32], ctypes.c_int),
+        "engram_history_reset": ([P, I32, U32, P], ctypes.c_int),
+        "engram_history_fork": ([P, P, I32, P], ctypes.c_int),
+        "engram_history_append": ([P, P, P, I32, I64, P, U32, U32, P, P], ctypes.c_int),
+        "engram_hash": ([P, P, I32, I64, P, P, U32, P, P, P, P], ctypes.c_int),
+        "engram_gather_decode": ([P, I64, P, P, U64, P, P, P], ctypes.c_int),
+        "engram_project": ([P, I64, P, I32, I32, P, P], ctypes.c_int),
+        "engram_gate": ([P, P, P, P, I64, I32, I32, F32, F32, P, P], ctypes.c_int),
+        "engram_forward_workspace": ([I64, I32, I32], SZ),
+        "engram_forward": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, P, I32, I32, F32, F32,
+                            P, SZ, P, P, P, P], ctypes.c_int),
+        "engram_gen_table": ([P, P, U64, U64, U64, U64, P], ctypes.c_int),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+lib = _load()
+
+
+def _status(s: int) -> str:
+    return lib.engram_status_string(s).decode()
+
+
+def _check(rc: int, fn: str) -> None:
+    if rc != ENGRAM_OK:
+        raise EngramError(rc, fn, lib.engram_last_error().decode())
+
+
+# ---------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtype=None, name="tensor", optional=False):
+    """Device pointer of a contiguous CUDA(HIP) tensor (or None -> NULL)."""
+    if t is None:
+        if optional:
+            return None
+        raise TypeError(f"{name} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _i32(torch):
+    return torch.int32
+
+
+def _u32(torch):
+    return (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def _u16(torch):
+    return (torch.int16, torch.bfloat16) + ((torch.uint16,) if hasattr(torch, "uint16") else ())
+
+
+# ---------------------------------------------------------------- entry points
+def engram_check_params(params, token_map: Optional[np.ndarray] = None) -> None:
+    """Host-only check of one layer's params (and host token map)."""
+    p = HashParams.from_any(params)
+    if token_map is None:
+        rc = lib.engram_check_params(ctypes.byref(p), None, 0)
+    else:
+        m = np.ascontiguousarray(token_map, dtype=np.uint32)
+        rc = lib.engram_check_params(ctypes.byref(p), m.ctypes.data, len(m))
+    _check(rc, "engram_check_params")
+
+
+def _need(t, n: int, name: str) -> None:
+    """A device buffer the kernels will touch n elements of must hold them."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, {n} needed")
+
+
+def _n_seqs(hist, name="hist") -> int:
+    """Sequences held by a history tensor of S*3 entries (any shape)."""
+    if hist.numel() % 3:
+        raise ValueError(f"{name} must hold S*3 entries (got {hist.numel()})")
+    return hist.numel() // 3
+
+
+def engram_history_reset(hist, pad_cid: int, stream=None) -> None:
+    torch = _torch()
+    S = _n_seqs(hist)
+    _check(lib.engram_history_reset(_ptr(hist, _u32(torch), "hist"), S, pad_cid, _stream(stream)),
+           "engram_history_reset")
+
+
+def engram_history_fork(dst, src, stream=None) -> None:
+    torch = _torch()
+    if dst.numel() != src.numel():
+        raise ValueError("dst and src histories differ in size")
+    _check(lib.engram_history_fork(_ptr(dst, _u32(torch), "dst"), _ptr(src, _u32(torch), "src"),
+                                   _n_seqs(dst, "dst"), _stream(stream)), "engram_history_fork")
+
+
+def engram_history_append(hist, tok, cu_seqlens, token_map, pad_cid: int, err_flags=None,
+                          stream=None) -> None:
+    torch = _torch()
+    S = cu_seqlens.numel() - 1
+    _need(hist, 3 * S, "hist")
+    _need(err_flags, 1, "err_flags")
+    _check(lib.engram_history_append(
+        _ptr(hist, _u32(torch), "hist"), _ptr(tok, _u32(torch), "tok"),
+        _ptr(cu_seqlens, _i32(torch), "cu_seqlens"), S, tok.numel(),
+        _ptr(token_map, _u32(torch), "token_map"), token_map.numel(), pad_cid,
+        _ptr(err_flags, _u32(torch), "err_flags", optional=True), _stream(stream)),
+        "engram_history_append")
+
+
+def engram_hash(tok, cu_seqlens, hist, token_map, params, idx, err_flags=None, stream=None) -> None:
+    torch = _torch()
+    p = HashParams.from_any(params)
+    S = cu_seqlens.numel() - 1
+    T = tok.numel()
+    if idx.numel() != T * BUCKETS:
+        raise ValueError("idx must hold T*24 entries")
+    _need(hist, 3 * S, "hist")
+    _need(err_flags, 1, "err_flags")
+    _check(lib.engram_hash(
+        _ptr(tok, _u32(torch), "tok"), _ptr(cu_seqlens, _i32(torch), "cu_seqlens"), S, T,
+        _ptr(hist, _u32(torch), "hist"), _ptr(token_map, _u32(torch), "token_map"),
+        token_map.numel(), ctypes.byref(p), _ptr(idx, _u32(torch), "idx"),
+        _ptr(err_flags, _u32(torch), "err_flags", optional=True), _stream(stream)), "engram_hash")
+
+
+def engram_gather_decode(idx, codes, scales, n_rows: int, mem, err_flags=None, stream=None) -> None:
+    torch = _torch()
+    T = idx.numel() // BUCKETS
+    if idx.numel() % BUCKETS or mem.numel() != T * MEM:
+        raise ValueError("idx must hold T*24 entries and mem T*6144")
+    _need(codes, n_rows * 256, "codes")
+    _need(scales, n_rows * 8, "scales")
+    _need(err_flags, 1, "err_flags")
+    _check(lib.engram_gather_decode(
+        _ptr(idx, _u32(torch), "idx"), T, _ptr(codes, torch.uint8, "codes"),
+        _ptr(scales, torch.uint8, "scales"), n_rows, _ptr(mem, _u16(torch), "mem"),
+        _ptr(err_flags, _u32(torch), "err_flags", optional=True), _stream(stream)),
+        "engram_gather_decode")
+
+
+def engram_project(mem, wkv, H: int, hc: int, kv, stream=None) -> None:
+    torch = _torch()
+    T = mem.numel() // MEM
+    if mem.numel() % MEM:
+        raise ValueError("mem must hold T*6144 entries")
+    if wkv.numel() != (hc + 1) * H * MEM or kv.numel() != T * (hc + 1) * H:
+        raise ValueError("wkv must be [(hc+1)*H][6144] and kv [T][(hc+1)*H]")
+    _check(lib.engram_project(_ptr(mem, _u16(torch), "mem"), T, _ptr(wkv, _u16(torch), "wkv"),
+                              H, hc, _ptr(kv, _u16(torch), "kv"), _stream(stream)),
+           "engram_project")
+
+
+def engram_gate(hidden, kv, wqk, tok, H: int, hc: int, eps: float = 1e-6, dot_scale: float = 1.0,
+                gate_out=None, stream=None) -> None:
+    torch = _torch()
+    T = hidden.numel() // (hc * H)
+    if hidden.numel() % (hc * H):
+        raise ValueError("hidden must hold T*hc*H entries")
+    if kv.numel() != T * (hc + 1) * H or wqk.numel() != hc * H:
+        raise ValueError("kv must be [T][(hc+1)*H] and wqk [hc][H]")
+    _need(tok, T, "tok")
+    _need(gate_out, T * hc, "gate_out")
+    _check(lib.engram_gate(
+        _ptr(hidden, _u16(torch), "hidden"), _ptr(kv, _u16(torch), "kv"),
+        _ptr(wqk, torch.float32, "wqk"), _ptr(tok, _u32(torch), "tok", optional=True), T, H, hc,
+        eps, dot_scale, _ptr(gate_out, torch.float32, "gate_out", optional=True), _stream(stream)),
+        "engram_gate")
+
+
+def engram_forward_workspace(T: int, H: int, hc: int) -> int:
+    return int(lib.engram_forward_workspace(T, H, hc))
+
+
+def engram_forward(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv, wqk, hidden,
+                   H: int, hc: int, eps: float = 1e-6, dot_scale: float = 1.0, ws=None,
+                   gate_out=None, err_flags=None, stage_events: Optional[Sequence] = None,
+                   stream=None):
+    """One Engram layer on the device. Returns the workspace tensor used
+    (idx, mem and k/v live in it; pass it back in to reuse it)."""
+    torch = _torch()
+    p = HashParams.from_any(params)
+    S = cu_seqlens.numel() - 1
+    T = tok.numel()
+    if hidden.numel() != T * hc * H:
+        raise ValueError("hidden must be [T][hc][H]")
+    if wkv.numel() != (hc + 1) * H * MEM or wqk.numel() != hc * H:
+        raise ValueError("wkv must be [(hc+1)*H][6144] and wqk [hc][H]")
+    _need(hist, 3 * S, "hist")
+    _need(codes, p.n_rows * 256, "codes")
+    _need(scales, p.n_rows * 8, "scales")
+    _need(gate_out, T * hc, "gate_out")
+    _need(err_flags, 1, "err_flags")
+    need = engram_forward_workspace(T, H, hc)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    _need(ws, need, "ws")
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {STAGE_EVENTS} events")
+        handles = [e.cuda_event for e in stage_events]
+        if not all(handles):
+            raise ValueError("stage_events: torch creates an event's HIP handle on its first "
+                             "record(); record each event once before passing it")
+        ev = (ctypes.c_void_p * STAGE_EVENTS)(*handles)
+    _check(lib.engram_forward(
+        _ptr(tok, _u32(torch), "tok"), _ptr(cu_seqlens, _i32(torch), "cu_seqlens"), S, T,
+        _ptr(hist, _u32(torch), "hist"), _ptr(token_map, _u32(torch), "token_map"),
+        token_map.numel(), ctypes.byref(p), _ptr(codes, torch.uint8, "codes"),
+        _ptr(scales, torch.uint8, "scales"), _ptr(wkv, _u16(torch), "wkv"),
+        _ptr(wqk, torch.float32, "wqk"), _ptr(hidden, _u16(torch), "hidden"), H, hc, eps,
+        dot_scale, _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _ptr(gate_out, torch.float32, "gate_out", optional=True),
+        _ptr(err_flags, _u32(torch), "err_flags", optional=True),
+        ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
+        "engram_forward")
+    return ws
+
+
+def engram_gen_table(codes, scales, row_begin: int, n_rows: int, key_data: int, key_scale: int,
+                     stream=None) -> None:
+    torch = _torch()
+    if codes.numel() < n_rows * 256 or scales.numel() < n_rows * 8:
+        raise ValueError("codes/scales too small for n_rows")
+    _check(lib.engram_gen_table(_ptr(codes, torch.uint8, "codes"), _ptr(scales, torch.uint8, "scales"),
+                                row_begin, n_rows, key_data, key_scale, _stream(stream)),
+           "engram_gen_table")

@@ -1,0 +1,50 @@
+// Internal declarations shared by the libengram sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/engram.h"
+
+namespace engram {
+
+// ---------------------------------------------------------------- launchers
+// Each launcher assumes the host-side checks in engram_api.cpp have passed
+// and returns the hipError_t of its launch.
+hipError_t launch_history_reset(uint32_t* hist, int32_t S, uint32_t pad_cid, hipStream_t st);
+hipError_t launch_history_copy(uint32_t* dst, const uint32_t* src, int32_t S, hipStream_t st);
+hipError_t launch_history_append(uint32_t* hist, const uint32_t* tok, const int32_t* cu,
+                                 int32_t S, int64_t T, const uint32_t* map, uint32_t map_len,
+                                 uint32_t pad_cid, uint32_t* err, hipStream_t st);
+hipError_t launch_hash(const uint32_t* tok, const int32_t* cu, int32_t S, int64_t T,
+                       const uint32_t* hist, const uint32_t* map, uint32_t map_len,
+                       const engram_hash_params& p, uint32_t* idx, uint32_t* err,
+                       hipStream_t st);
+hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
+                                const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
+                                uint32_t* err, hipStream_t st);
+hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
+                          uint16_t* kv, hipStream_t st);
+hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
+                       const uint32_t* tok, int64_t T, int32_t H, int32_t hc, float eps,
+                       float dot_scale, float* gate_out, hipStream_t st);
+hipError_t launch_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin,
+                            uint64_t n_rows, uint64_t key_data, uint64_t key_scale,
+                            hipStream_t st);
+
+// ---------------------------------------------------------------- device helpers
+// float32 -> bfloat16 bits, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  __bf16 b = static_cast<__bf16>(x);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ void set_err(uint32_t* err, uint32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+}  // namespace engram

@@ -1,0 +1,220 @@
+/*
+ * engram.h - C ABI of libengram, the MI355X (gfx950) Engram forward path.
+ *
+ * Engram is a conditional-memory layer: each position hashes its recent
+ * compressed tokens into a large static table, gathers the selected rows,
+ * projects them to keys and a value, and gates the value into the hidden
+ * state. Sources (web pages on Engram):
+ *   [zLLM]    zhuai.tech, "DeepSeek V4.1 Flash 的 Engram：让知识不必每次重新算"
+ *   [Storage] lqnn.cn, "3.84 亿行 Embedding 的存法大揭秘"
+ *   [vLLM]    data-sketchers.com wiki, "Engram: n-gram 조회를 통한 조건부 메모리"
+ *
+ * Conventions for every entry point:
+ *  - Array pointers are DEVICE pointers owned by the caller. The library never
+ *    allocates or frees memory the caller sees, keeps no state between calls
+ *    and never synchronises the host with the device.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    at once. Calls are thread-safe.
+ *  - BF16 values travel as uint16_t bit patterns.
+ *  - Shapes, pointers, alignment and parameter tables are checked on the host
+ *    before anything is launched; a failed check returns ENGRAM_EINVAL and
+ *    launches nothing (engram_last_error() says which check failed).
+ *  - Violations the host cannot see without reading device memory (a token
+ *    id >= map_len, a map value >= vocab_c, a row index >= n_rows,
+ *    cu_seqlens that are not a non-decreasing list from 0 to T) never cause
+ *    an out-of-bounds access. If `err_flags` is non-NULL the kernels OR the
+ *    ENGRAM_ERR_* bits into it; the affected outputs are then unspecified
+ *    but written in bounds.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENGRAM_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+#define ENGRAM_OK            0
+#define ENGRAM_EINVAL       (-1)  /* host-side shape, pointer, alignment or parameter check failed */
+#define ENGRAM_EHIP         (-2)  /* a HIP launch or runtime call failed */
+#define ENGRAM_EUNSUPPORTED (-3)  /* valid request this build does not handle (e.g. not gfx950) */
+
+/* Device-side error bits (ORed into *err_flags when err_flags != NULL). */
+#define ENGRAM_ERR_TOKEN_RANGE 0x1u  /* a non-DEAD token id >= map_len (hashed as pad_cid) */
+#define ENGRAM_ERR_MAP_RANGE   0x2u  /* a token map value >= vocab_c */
+#define ENGRAM_ERR_ROW_RANGE   0x4u  /* a row index >= n_rows that is not ENGRAM_DEAD_IDX (row written as 0) */
+#define ENGRAM_ERR_SEQLENS     0x8u  /* cu_seqlens not non-decreasing from 0 to T */
+
+/* Fixed geometry: 2/3/4-grams x 8 heads = 24 rows of 256 values per token
+ * per layer, 3 x 8 x 256 = 6,144 memory values ([zLLM] 把知识变成可寻址的向量). */
+#define ENGRAM_BUCKETS        24
+#define ENGRAM_HEADS_PER_ORDER 8
+#define ENGRAM_ROW            256
+#define ENGRAM_SCALES_PER_ROW 8      /* one E8M0 scale per 32 values ([zLLM] 第二步) */
+#define ENGRAM_MEM            6144
+#define ENGRAM_HIST           3      /* history slots: the three most recent compressed ids */
+
+#define ENGRAM_DEAD_TOKEN 0xFFFFFFFFu /* token value of an image (DEAD) position ([zLLM] 第四步) */
+#define ENGRAM_DEAD_IDX   0xFFFFFFFFu /* row index written for a DEAD position */
+
+/* One layer's hash parameters ([zLLM] 第一步: per-layer multipliers, prime
+ * buckets and bucket offsets expanded to static tables; [vLLM] How it works:
+ * each (order, head) pair indexes its own prime-sized bucket range).
+ * Bucket j = (n-2)*8 + head has order n = 2 + j/8. Passed by pointer to a
+ * HOST struct; it is copied into the kernel arguments. */
+typedef struct {
+  uint64_t mult[ENGRAM_BUCKETS][4]; /* multiplier of window slot k (k < n) for bucket j */
+  uint32_t prime[ENGRAM_BUCKETS];   /* bucket sizes: distinct primes */
+  uint64_t offset[ENGRAM_BUCKETS];  /* offset[0] = 0, offset[j+1] = offset[j] + prime[j] */
+  uint64_t n_rows;                  /* offset[23] + prime[23]; must be < 0xFFFFFFFF */
+  uint32_t vocab_c;                 /* compressed vocabulary size */
+  uint32_t pad_cid;                 /* id hashed for history slots before the start or behind a DEAD */
+} engram_hash_params;
+
+/* Number of hipEvent_t handles engram_forward records when given events. */
+#define ENGRAM_STAGE_EVENTS 5
+
+/* ---------------------------------------------------------------- status */
+
+/* Static text for a status code. Never NULL. */
+const char* engram_status_string(int status);
+
+/* Detail of the last ENGRAM_EINVAL / ENGRAM_EHIP returned on this thread
+ * (empty string if none). Valid until the next call on this thread. */
+const char* engram_last_error(void);
+
+/* ENGRAM_ABI_VERSION of the built library. */
+int engram_abi_version(void);
+
+/* ---------------------------------------------------------------- parameters */
+
+/* Pure host check of one layer's parameters against its token map
+ * ([vLLM] How it works: a compressed-vocabulary mismatch must fail at
+ * start-up). Checks: every prime[j] is prime and the 24 are distinct; the
+ * offsets are the prefix sums of the primes, so bucket ranges are disjoint
+ * and tile [0, n_rows); n_rows < 0xFFFFFFFF; vocab_c >= 1; pad_cid <
+ * vocab_c; every token_map_host[i] < vocab_c. token_map_host is a HOST
+ * array of map_len entries (may be NULL when map_len == 0). No GPU needed. */
+int engram_check_params(const engram_hash_params* params,
+                        const uint32_t* token_map_host, uint32_t map_len);
+
+/* ---------------------------------------------------------------- history
+ * Per-sequence hash history: hist[S][3] uint32 compressed ids, hist[s][0] the
+ * most recent. Each token enters the history exactly once per step, after
+ * every Engram layer of that step has read it; sessions share weights but
+ * not history; fork copies, reset clears ([zLLM] 第四步). */
+
+/* hist[s][*] = pad_cid for s < S. */
+int engram_history_reset(uint32_t* hist, int32_t S, uint32_t pad_cid, hipStream_t stream);
+
+/* dst[s][*] = src[s][*] for s < S (a forked session's own copy). */
+int engram_history_fork(uint32_t* dst, const uint32_t* src, int32_t S, hipStream_t stream);
+
+/* Append one step's tokens. Sequence s owns tokens [cu_seqlens[s],
+ * cu_seqlens[s+1]) of tok[T] (cu_seqlens: int32[S+1], 0 = cu[0] <= ... <=
+ * cu[S] = T; empty sequences allowed). For each token in order: a DEAD
+ * token resets the history to pad_cid; any other token t pushes
+ * map[t] (hist becomes [map[t], h0, h1]). In place; sequences independent. */
+int engram_history_append(uint32_t* hist, const uint32_t* tok, const int32_t* cu_seqlens,
+                          int32_t S, int64_t T, const uint32_t* token_map, uint32_t map_len,
+                          uint32_t pad_cid, uint32_t* err_flags, hipStream_t stream);
+
+/* ---------------------------------------------------------------- stages */
+
+/* Hash (retrieval, first half): idx[T][24] uint32 row numbers.
+ * Window of a text token t: [c_t, h0, h1, h2] where c_t = token_map[tok[t]]
+ * and h is the history just before t within its sequence (the read-only
+ * `hist` before the first token; pad_cid behind a DEAD) ([zLLM] 第一步).
+ * Bucket j of order n: x = XOR_{k<n} (w_k * mult[j][k] mod 2^64),
+ * idx[t][j] = offset[j] + x mod prime[j] ([vLLM] How it works, multi-head
+ * hashing). DEAD tokens get ENGRAM_DEAD_IDX in all 24 slots. `hist` is not
+ * modified (call engram_history_append once per step, after all layers).
+ * Alignment: tok, idx, hist, cu_seqlens 4-byte. T may be 0. */
+int engram_hash(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                const engram_hash_params* params, uint32_t* idx,
+                uint32_t* err_flags, hipStream_t stream);
+
+/* Gather + decode (retrieval, second half): mem[T][6144] BF16.
+ * mem[t][j*256 + c] = E4M3(codes[r][c]) * 2^(scales[r][c/32] - 127) with
+ * r = idx[t][j], rounded to BF16 (nearest even; exact for every finite value
+ * with |v| >= 2^-133); NaN (code S.1111.111 or scale 255) gives
+ * sign(code)|0x7FC0 ([zLLM] 第二步: read only the selected rows and their
+ * scales; [Storage]: FP8 E4M3 with UE8M0 group-32 scales decoded to BF16).
+ * ENGRAM_DEAD_IDX rows give zeros. codes: uint8[n_rows][256] (16-byte
+ * aligned), scales: uint8[n_rows][8] (8-byte aligned), mem 16-byte aligned. */
+int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
+                         const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
+                         uint32_t* err_flags, hipStream_t stream);
+
+/* wkv projection: kv[T][(hc+1)*H] = mem[T][6144] . wkv[(hc+1)*H][6144]^T,
+ * BF16 inputs, FP32 accumulation, BF16 (nearest even) output. Columns
+ * [b*H, (b+1)*H) of kv are key b (b < hc); [hc*H, (hc+1)*H) the shared value
+ * ([zLLM] 第二步: wkv 25,600 x 6,144 BF16; [Storage] 旋转合同: the last 5,120
+ * rows are V; [vLLM] How it works: one key per hyper-connection branch and
+ * one shared value). Requires H % 64 == 0, 1 <= hc <= 8, 16-byte aligned
+ * pointers. T may be 0. */
+int engram_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t H, int32_t hc,
+                   uint16_t* kv, hipStream_t stream);
+
+/* Context gate + residual, in place on hidden[T][hc][H] BF16.
+ * For each non-DEAD token and branch b (DEAD = tok[t] == ENGRAM_DEAD_TOKEN,
+ * tok may be NULL for no DEAD positions):
+ *   r_h = 1/sqrt(mean(h_b^2) + eps), r_k = 1/sqrt(mean(k_b^2) + eps)
+ *   dot = dot_scale * r_h * r_k * sum_i h_b[i] * k_b[i] * wqk[b][i]
+ *   g   = sigmoid(copysign(sqrt(max(|dot|, 1e-6)), dot))
+ *   h_b = bf16(h_b + g * v)
+ * ([zLLM] 第三步; [vLLM] How it works, fusion). DEAD rows are left
+ * bit-identical and get g = 0 ([zLLM] 第四步: image rows skip the gate).
+ * wqk: float32[hc][H] (premultiplied q and k norm weights). gate_out:
+ * float32[T][hc] or NULL. Requires H % 64 == 0, 1 <= hc <= 8, 16-byte
+ * aligned hidden/kv/wqk. */
+int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const uint32_t* tok,
+                int64_t T, int32_t H, int32_t hc, float eps, float dot_scale,
+                float* gate_out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- whole layer */
+
+/* Workspace bytes engram_forward needs for T tokens (idx, mem and k/v). */
+size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
+
+/* One Engram layer: engram_hash -> engram_gather_decode -> engram_project ->
+ * engram_gate, enqueued on one stream, intermediates in `ws` (caller-owned
+ * device memory of at least engram_forward_workspace(T, H, hc) bytes,
+ * 256-byte aligned). Arguments mean what they mean in the stage calls.
+ * Per step: call once per layer with that layer's params/table/wkv/wqk and
+ * hidden, all reading the same `hist`, then engram_history_append once.
+ * stage_events: NULL, or ENGRAM_STAGE_EVENTS hipEvent_t created by the caller,
+ * recorded before hashing, after hashing, after gather+decode, after the
+ * projection and after the gate. */
+int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                   const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                   const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,
+                   const uint16_t* wkv, const float* wqk, uint16_t* hidden, int32_t H, int32_t hc,
+                   float eps, float dot_scale, void* ws, size_t ws_bytes, float* gate_out,
+                   uint32_t* err_flags, hipEvent_t* stage_events, hipStream_t stream);
+
+/* ---------------------------------------------------------------- synthetic tables */
+
+/* Writes rows [row_begin, row_begin + n_rows) of a closed-form synthetic
+ * MXFP8 table, for benchmarks and tests (not part of the Engram method):
+ *   codes[r][c]  = F[hi32(splitmix64(key_data + r*256 + c)) mod 254]
+ *   scales[r][q] = 119 + hi32(splitmix64(key_scale + r*8 + q)) mod 9
+ * where F lists the 254 non-NaN E4M3 codes in ascending order and
+ * splitmix64(x) is the first output of a SplitMix64 generator (Steele, Lea
+ * and Flood, 2014) whose state is x. `codes` and `scales` point at row
+ * row_begin (16- and 8-byte aligned). */
+int engram_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin, uint64_t n_rows,
+                     uint64_t key_data, uint64_t key_scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

@@ -1,0 +1,88 @@
+"""Shared helpers of the GPU parity tests: device upload/download of the
+seeded inputs, the tolerance checks, and per-config worlds."""
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import List
+
+import numpy as np
+import torch
+
+import engram_synth as synth
+from oracle import engram_oracle as O
+
+DEV = "cuda"
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def up32(a: np.ndarray) -> torch.Tensor:
+    """uint32/int32 host array -> int32 device tensor (same bits)."""
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int32) if a.dtype == np.uint32 else a.astype(np.int32)).to(DEV)
+
+
+def up16(a: np.ndarray) -> torch.Tensor:
+    """uint16 bit patterns -> int16 device tensor (same bits)."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(DEV)
+
+
+def upf(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def up8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
+
+
+def down32(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def down16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def assert_bf16_close(got: np.ndarray, ref: np.ndarray, rel: float = 2e-2, what: str = "") -> None:
+    """|got - ref| <= rel * max(|ref|, rms(ref row)) elementwise (BF16 bits in,
+    rows along the last axis)."""
+    g = O.bf16_to_f64(got)
+    r = O.bf16_to_f64(ref)
+    rms = np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
+    bound = rel * np.maximum(np.abs(r), rms)
+    bad = ~(np.abs(g - r) <= bound)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at "
+                             f"{tuple(i)}: got {g[tuple(i)]!r} ref {r[tuple(i)]!r}")
+
+
+@dataclasses.dataclass
+class World:
+    """Host inputs of one config and layer (small enough to hold on the host)."""
+    cfg: synth.Config
+    tmap: np.ndarray
+    params: List[synth.HashParams]
+    keys: List[tuple]
+
+    @classmethod
+    def of(cls, name: str) -> "World":
+        cfg = synth.CONFIGS[name]
+        tmap = synth.make_token_map(cfg.root, cfg.map_len, cfg.vocab_c)
+        return cls(cfg, tmap, synth.params_for(cfg),
+                   [synth.table_keys(cfg.root, l) for l in cfg.layers])
+
+    def rows(self, li: int):
+        kd, ks = self.keys[li]
+        return lambda r: synth.table_rows(r, kd, ks)
+
+
+def device_table(E, n_rows: int, key_data: int, key_scale: int):
+    codes = torch.empty(n_rows * 256, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(n_rows * 8, dtype=torch.uint8, device=DEV)
+    E.engram_gen_table(codes, scales, 0, n_rows, key_data, key_scale)
+    return codes, scales

@@ -1,0 +1,137 @@
+"""The C ABI: the built library loads, exports every entry point the header
+declares, and its host-side checks reject bad input (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import engram_synth as synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "engram.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(engram_\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def E():
+    import gram_hashed_embedding_amd as E
+    return E
+
+
+def test_header_declares_the_stage_entry_points():
+    names = _declared()
+    for n in ("engram_hash", "engram_gather_decode", "engram_project", "engram_gate",
+              "engram_forward", "engram_history_append", "engram_history_fork",
+              "engram_history_reset", "engram_check_params", "engram_forward_workspace"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(E):
+    out = subprocess.run(["nm", "-D", "--defined-only", E.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (engram_\w+)$", out, flags=re.M))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        assert hasattr(E.lib, n)
+    assert E.lib.engram_abi_version() == 1
+
+
+def test_status_strings(E):
+    for s in (0, -1, -2, -3, 7):
+        assert E.lib.engram_status_string(s)
+
+
+def _params(name="tiny"):
+    cfg = synth.CONFIGS[name]
+    return synth.params_for(cfg)[0], synth.make_token_map(cfg.root, cfg.map_len, cfg.vocab_c)
+
+
+def test_check_params_accepts_the_configs(E):
+    for name in ("tiny", "decode", "full", "long"):
+        cfg = synth.CONFIGS[name]
+        tmap = synth.make_token_map(cfg.root, cfg.map_len, cfg.vocab_c)
+        for p in synth.params_for(cfg):
+            E.engram_check_params(p, tmap)
+
+
+def _hp(E, p, **over):
+    h = E.HashParams.from_any(p)
+    for k, v in over.items():
+        setattr(h, k, v)
+    return h
+
+
+@pytest.mark.parametrize("case", ["not_prime", "duplicate", "offset", "n_rows", "too_many_rows",
+                                  "vocab0", "pad", "map_value"])
+def test_check_params_rejects(E, case):
+    p, tmap = _params()
+    h = E.HashParams.from_any(p)
+    m = tmap.copy()
+    if case == "not_prime":
+        h.prime[3] = 1001
+    elif case == "duplicate":
+        h.prime[4] = h.prime[3]
+    elif case == "offset":
+        h.offset[5] += 1
+    elif case == "n_rows":
+        h.n_rows += 1
+    elif case == "too_many_rows":
+        for j in range(24):
+            h.prime[j] = 4294967291 if j == 23 else h.prime[j]
+        h.n_rows = int(h.offset[23]) + 4294967291
+    elif case == "vocab0":
+        h.vocab_c = 0
+    elif case == "pad":
+        h.pad_cid = h.vocab_c
+    elif case == "map_value":
+        m[17] = p.vocab_c
+    with pytest.raises(E.EngramError) as ei:
+        E.engram_check_params(h, m)
+    assert ei.value.status == -1
+    assert E.lib.engram_last_error().decode()
+
+
+def test_stage_entry_points_reject_bad_shapes_before_launch(E):
+    """Host checks fire without touching a device (NULL stream, fake pointers
+    are never dereferenced because validation fails first)."""
+    L = E.lib
+    p, _ = _params()
+    hp = E.HashParams.from_any(p)
+    fake = ctypes.c_void_p(0x10000)
+    # H not a multiple of 64
+    assert L.engram_project(fake, 4, fake, 100, 4, fake, None) == -1
+    assert b"multiple of 64" in L.engram_last_error()
+    # hc out of range
+    assert L.engram_gate(fake, fake, fake, None, 4, 256, 9, 1e-6, 1.0, None, None) == -1
+    # misaligned operand
+    assert L.engram_project(ctypes.c_void_p(0x10002), 4, fake, 256, 4, fake, None) == -1
+    # tokens without sequences
+    assert L.engram_hash(fake, fake, 0, 5, fake, fake, 10, ctypes.byref(hp), fake, None, None) == -1
+    # workspace too small
+    need = L.engram_forward_workspace(8, 256, 4)
+    assert need > 0
+    rc = L.engram_forward(fake, fake, 1, 8, fake, fake, 10, ctypes.byref(hp), fake, fake, fake,
+                          fake, fake, 256, 4, 1e-6, 1.0, fake, need - 1, None, None, None, None)
+    assert rc == -1 and b"workspace" in L.engram_last_error()
+    # bad params struct is caught by engram_hash too
+    hp.prime[0] = 4
+    assert L.engram_hash(fake, fake, 1, 5, fake, fake, 10, ctypes.byref(hp), fake, None, None) == -1
+    # empty calls are no-ops that succeed without a device
+    assert L.engram_gather_decode(None, 0, None, None, 0, None, None, None) == 0
+    assert L.engram_project(None, 0, None, 256, 4, None, None) == 0
+
+
+def test_workspace_size_formula(E):
+    T, H, hc = 1000, 5120, 4
+    r = lambda x: (x + 255) // 256 * 256
+    assert E.engram_forward_workspace(T, H, hc) == r(T * 96) + r(T * 12288) + r(T * 25600 * 2)
+    assert E.engram_forward_workspace(0, H, hc) == 0

@@ -1,0 +1,356 @@
+"""GPU parity of every stage against the oracle at sizes the oracle finishes
+in seconds (several tiles plus ragged tails), through the C ABI.
+
+Bars: hash indices, decoded rows, history and tables bit-exact; k/v and
+hidden within 2e-2 * max(|ref|, rms(ref row)); gate within 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import engram_synth as synth
+from oracle import engram_oracle as O
+from tests.conftest import gpu_available
+from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, down32, log,
+                               up8, up16, up32, upf)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
+
+
+@pytest.fixture(scope="module")
+def E():
+    import gram_hashed_embedding_amd as E
+    return E
+
+
+def _gpu_hash(E, tok, cu, hist, tmap, p, err=None):
+    T = len(tok)
+    idx = torch.empty(T * 24, dtype=torch.int32, device=DEV)
+    E.engram_hash(up32(tok), up32(cu), up32(hist), up32(tmap), p, idx, err_flags=err)
+    return down32(idx).reshape(T, 24)
+
+
+def _ref_hash(tok, cu, hist, tmap, p):
+    win, dead, _ = O.walk(tok, cu, hist, tmap, p.pad_cid)
+    return O.hash_windows(win, dead, p.mult, p.prime, p.offset)
+
+
+# ---------------------------------------------------------------- tables
+def test_gen_table_matches_the_closed_form(E):
+    log("gen_table: tiny table, and rows at an offset")
+    w = World.of("tiny")
+    n = w.params[0].n_rows
+    kd, ks = w.keys[0]
+    codes, scales = device_table(E, n, kd, ks)
+    rc, rs = synth.table_rows(np.arange(n, dtype=np.uint64), kd, ks)
+    assert np.array_equal(codes.cpu().numpy().reshape(n, 256), rc)
+    assert np.array_equal(scales.cpu().numpy().reshape(n, 8), rs)
+    # a window of rows deep inside a 384M-row table, written through row_begin
+    begin, cnt = 384_006_168 - 1000, 1000
+    c2 = torch.empty(cnt * 256, dtype=torch.uint8, device=DEV)
+    s2 = torch.empty(cnt * 8, dtype=torch.uint8, device=DEV)
+    E.engram_gen_table(c2, s2, begin, cnt, kd, ks)
+    rc, rs = synth.table_rows(np.arange(begin, begin + cnt, dtype=np.uint64), kd, ks)
+    assert np.array_equal(c2.cpu().numpy().reshape(cnt, 256), rc)
+    assert np.array_equal(s2.cpu().numpy().reshape(cnt, 8), rs)
+
+
+# ---------------------------------------------------------------- decode
+def test_decode_exhaustive_code_scale_grid(E):
+    """Row r holds all 256 codes with every scale = r, so gathering rows
+    0..255 decodes every (code, scale) pair, NaN and subnormals included."""
+    log("gather_decode: exhaustive 256 x 256 (code, scale)")
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 8, axis=1)
+    T = 11
+    idx = np.full(T * 24, O.DEAD_IDX, dtype=np.uint32)
+    idx[:256] = np.arange(256)
+    mem = torch.empty(T * 6144, dtype=torch.int16, device=DEV)
+    E.engram_gather_decode(up32(idx), up8(codes), up8(scales), 256, mem)
+    got = down16(mem).reshape(T * 24, 256)
+    ref = O.bf16_rne(O.decode_rows(codes, scales))
+    assert np.array_equal(got[:256], ref)
+    assert np.all(got[256:] == 0)                    # DEAD rows give zeros
+
+
+def test_gather_decode_tiny_and_error_flags(E):
+    log("gather_decode: tiny config")
+    w = World.of("tiny")
+    p = w.params[0]
+    tok, cu = synth.token_batch(w.cfg)
+    hist = O.history_reset(1, p.pad_cid)
+    idx = _ref_hash(tok, cu, hist, w.tmap, p)
+    idx[7] = O.DEAD_IDX
+    kd, ks = w.keys[0]
+    codes, scales = device_table(E, p.n_rows, kd, ks)
+    mem = torch.empty(len(tok) * 6144, dtype=torch.int16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    E.engram_gather_decode(up32(idx), codes, scales, p.n_rows, mem, err_flags=err)
+    ref = O.gather_decode(idx, w.rows(0))
+    assert np.array_equal(down16(mem).reshape(-1, 6144), ref)
+    assert int(err.item()) == 0
+    bad = idx.copy()
+    bad[3, 5] = p.n_rows + 2                          # beyond the table: flagged, row zeroed
+    E.engram_gather_decode(up32(bad), codes, scales, p.n_rows, mem, err_flags=err)
+    assert int(err.item()) & 0x4
+    got = down16(mem).reshape(-1, 24, 256)
+    assert np.all(got[3, 5] == 0)
+    assert np.array_equal(got[3, 4], ref.reshape(-1, 24, 256)[3, 4])
+
+
+# ---------------------------------------------------------------- hashing and history
+def test_hash_tiny(E):
+    log("hash: tiny config")
+    w = World.of("tiny")
+    p = w.params[0]
+    tok, cu = synth.token_batch(w.cfg)
+    hist = O.history_reset(1, p.pad_cid)
+    assert np.array_equal(_gpu_hash(E, tok, cu, hist, w.tmap, p), _ref_hash(tok, cu, hist, w.tmap, p))
+
+
+def _ragged_batch(seed, lens, map_len, vocab_c, dead_spans=True):
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    tok = synth.zipf_tokens(rng, int(cu[-1]), map_len)
+    if dead_spans:
+        for s, L in enumerate(lens):
+            if L >= 8:
+                a = int(cu[s]) + int(rng.integers(1, L - 3))
+                tok[a: a + int(rng.integers(1, 3))] = O.DEAD_TOKEN
+        tok[int(cu[-1]) - 1] = O.DEAD_TOKEN            # a DEAD as the very last token
+    hist = rng.integers(0, vocab_c, (len(lens), 3)).astype(np.uint32)
+    return tok, cu, hist
+
+
+def test_hash_ragged_sequences_dead_and_history(E):
+    log("hash: ragged multi-sequence batch with DEAD spans and carried history")
+    w = World.of("decode")
+    p = w.params[0]
+    tok, cu, hist = _ragged_batch(1, [0, 1, 2, 3, 5, 37, 300, 0, 4000], w.cfg.map_len, p.vocab_c)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = _gpu_hash(E, tok, cu, hist, w.tmap, p, err)
+    assert np.array_equal(got, _ref_hash(tok, cu, hist, w.tmap, p))
+    assert int(err.item()) == 0
+
+
+def test_hash_long_prefill_both_layers(E):
+    log("hash: 50,032-token prefill, layers 1 and 14")
+    w = World.of("long")
+    tok, cu = synth.token_batch(w.cfg)
+    for p in w.params:
+        hist = O.history_reset(1, p.pad_cid)
+        assert np.array_equal(_gpu_hash(E, tok, cu, hist, w.tmap, p), _ref_hash(tok, cu, hist, w.tmap, p))
+
+
+def test_hash_flags_out_of_range_tokens(E):
+    w = World.of("tiny")
+    p = w.params[0]
+    tok = np.array([1, 2, 4096, 3], dtype=np.uint32)        # 4096 >= map_len
+    cu = np.array([0, 4], np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    _gpu_hash(E, tok, cu, O.history_reset(1, p.pad_cid), w.tmap, p, err)
+    assert int(err.item()) & 0x1
+
+
+def test_history_append_fork_reset(E):
+    log("history: append / fork / reset over several steps")
+    w = World.of("decode")
+    p = w.params[0]
+    lens = [0, 1, 2, 3, 4, 9, 50, 1]
+    S = len(lens)
+    hist_d = torch.empty(S * 3, dtype=torch.int32, device=DEV)
+    E.engram_history_reset(hist_d, p.pad_cid)
+    ref = O.history_reset(S, p.pad_cid)
+    assert np.array_equal(down32(hist_d).reshape(S, 3), ref)
+    tmap_d = up32(w.tmap)
+    for step in range(4):
+        tok, cu, _ = _ragged_batch(10 + step, lens, w.cfg.map_len, p.vocab_c)
+        E.engram_history_append(hist_d, up32(tok), up32(cu), tmap_d, p.pad_cid)
+        ref = O.history_append(ref, tok, cu, w.tmap, p.pad_cid)
+        assert np.array_equal(down32(hist_d).reshape(S, 3), ref), step
+    child = torch.empty_like(hist_d)
+    E.engram_history_fork(child, hist_d)
+    parent_before = down32(hist_d).copy()
+    tok, cu, _ = _ragged_batch(99, lens, w.cfg.map_len, p.vocab_c)
+    E.engram_history_append(child, up32(tok), up32(cu), tmap_d, p.pad_cid)
+    assert np.array_equal(down32(hist_d), parent_before)
+    assert np.array_equal(down32(child).reshape(S, 3),
+                          O.history_append(parent_before.reshape(S, 3), tok, cu, w.tmap, p.pad_cid))
+
+
+# ---------------------------------------------------------------- projection
+def _mem_from_tiny(T, seed=0):
+    w = World.of("tiny")
+    p = w.params[0]
+    rng = np.random.default_rng(seed)
+    tok = rng.integers(0, w.cfg.map_len, T).astype(np.uint32)
+    cu = np.array([0, T], np.int32)
+    idx = _ref_hash(tok, cu, O.history_reset(1, p.pad_cid), w.tmap, p)
+    return O.gather_decode(idx, w.rows(0))
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 300])
+def test_project_tiny_widths(E, T):
+    log(f"project: tiny wkv (1,280 x 6,144), T={T}")
+    cfg = synth.CONFIGS["tiny"]
+    wkv = synth.wkv_bf16(cfg, 1)
+    mem = _mem_from_tiny(T, seed=T)
+    kv = torch.empty(T * 1280, dtype=torch.int16, device=DEV)
+    E.engram_project(up16(mem), up16(wkv), cfg.H, cfg.hc, kv)
+    assert_bf16_close(down16(kv).reshape(T, -1), O.project(mem, wkv), what="kv")
+
+
+def test_project_one_hot_is_exact(E):
+    cfg = synth.CONFIGS["tiny"]
+    wkv = synth.wkv_bf16(cfg, 1)
+    T = 70
+    mem = np.zeros((T, 6144), np.uint16)
+    cols = np.random.default_rng(0).integers(0, 6144, T)
+    mem[np.arange(T), cols] = 0x3F80
+    kv = torch.empty(T * 1280, dtype=torch.int16, device=DEV)
+    E.engram_project(up16(mem), up16(wkv), cfg.H, cfg.hc, kv)
+    assert np.array_equal(down16(kv).reshape(T, -1), wkv[:, cols].T)
+
+
+def test_project_ragged_n(E):
+    """N = (hc+1)*H = 192 is not a multiple of the 128-wide tile."""
+    rng = np.random.default_rng(5)
+    H, hc, T = 64, 2, 130
+    wkv = synth.bf16_bits_from_f32(0.02 * rng.standard_normal(((hc + 1) * H, 6144)).astype(np.float32))
+    mem = synth.bf16_bits_from_f32(rng.standard_normal((T, 6144)).astype(np.float32))
+    kv = torch.empty(T * (hc + 1) * H, dtype=torch.int16, device=DEV)
+    E.engram_project(up16(mem), up16(wkv), H, hc, kv)
+    assert_bf16_close(down16(kv).reshape(T, -1), O.project(mem, wkv), what="kv")
+
+
+@pytest.mark.parametrize("T", [64, 257])
+def test_project_full_width(E, T):
+    log(f"project: full wkv 25,600 x 6,144, T={T}")
+    cfg = synth.CONFIGS["decode"]
+    wkv = synth.wkv_bf16(cfg, 1)
+    mem = synth.bf16_bits_from_f32(
+        np.random.default_rng(T).standard_normal((T, 6144)).astype(np.float32) * 0.1)
+    kv = torch.empty(T * 25600, dtype=torch.int16, device=DEV)
+    E.engram_project(up16(mem), up16(wkv), cfg.H, cfg.hc, kv)
+    assert_bf16_close(down16(kv).reshape(T, -1), O.project(mem, wkv), what="kv")
+
+
+# ---------------------------------------------------------------- gate
+@pytest.mark.parametrize("dot_scale", [1.0, 1 / 16.0])
+@pytest.mark.parametrize("H,hc", [(256, 4), (64, 1), (5120, 4), (128, 8)])
+def test_gate_identical_inputs(E, H, hc, dot_scale):
+    log(f"gate: H={H} hc={hc} dot_scale={dot_scale}")
+    T = 67
+    rng = np.random.default_rng(H + hc)
+    hidden = synth.bf16_bits_from_f32(rng.standard_normal((T, hc, H)).astype(np.float32))
+    kv = synth.bf16_bits_from_f32(rng.standard_normal((T, (hc + 1) * H)).astype(np.float32))
+    # a few rows whose key equals hidden (large positive dot) or its negation
+    kv[1, : hc * H] = hidden[1].reshape(-1)
+    kv[2, : hc * H] = hidden[2].reshape(-1) ^ 0x8000
+    wqk = (1 + 0.1 * rng.standard_normal((hc, H))).astype(np.float32)
+    tok = rng.integers(0, 1000, T).astype(np.uint32)
+    tok[[0, 5, 6, T - 1]] = O.DEAD_TOKEN
+    dead = tok == O.DEAD_TOKEN
+    h_d = up16(hidden)
+    g_d = torch.empty(T * hc, dtype=torch.float32, device=DEV)
+    E.engram_gate(h_d, up16(kv), upf(wqk), up32(tok), H, hc, 1e-6, dot_scale, gate_out=g_d)
+    new, g, _ = O.gate_residual(hidden, kv, wqk, dead, H, hc, 1e-6, dot_scale)
+    got_g = g_d.cpu().numpy().reshape(T, hc)
+    assert np.max(np.abs(got_g - g)) <= 1e-3
+    got_h = down16(h_d).reshape(T, hc, H)
+    assert np.array_equal(got_h[dead], hidden[dead])          # DEAD rows bit-identical
+    assert np.all(got_g[dead] == 0)
+    assert_bf16_close(got_h.reshape(T * hc, H), new.reshape(T * hc, H), what="hidden")
+
+
+def test_gate_without_dead_mask_and_zero_value(E):
+    H, hc, T = 256, 4, 9
+    rng = np.random.default_rng(3)
+    hidden = synth.bf16_bits_from_f32(rng.standard_normal((T, hc, H)).astype(np.float32))
+    kv = synth.bf16_bits_from_f32(rng.standard_normal((T, (hc + 1) * H)).astype(np.float32))
+    kv[:, hc * H:] = 0
+    h_d = up16(hidden)
+    E.engram_gate(h_d, up16(kv), upf(np.ones((hc, H), np.float32)), None, H, hc)
+    assert np.array_equal(down16(h_d).reshape(T, hc, H), hidden)
+
+
+# ---------------------------------------------------------------- whole layer
+def _run_forward(E, w, li, tok, cu, hist, hidden, dot_scale=1.0):
+    cfg, p = w.cfg, w.params[li]
+    kd, ks = w.keys[li]
+    codes, scales = device_table(E, p.n_rows, kd, ks)
+    wkv = synth.wkv_bf16(cfg, cfg.layers[li])
+    wqk = synth.norm_weights(cfg, cfg.layers[li])
+    T = len(tok)
+    h_d = up16(hidden)
+    g_d = torch.empty(T * cfg.hc, dtype=torch.float32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = E.engram_forward(up32(tok), up32(cu), up32(hist), up32(w.tmap), p, codes, scales,
+                          up16(wkv), upf(wqk), h_d, cfg.H, cfg.hc, 1e-6, dot_scale,
+                          gate_out=g_d, err_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    nb = (T * 96 + 255) // 256 * 256
+    idx = down32(ws[: T * 96].view(torch.int32)).reshape(T, 24)
+    mem = down16(ws[nb: nb + T * 12288].view(torch.int16)).reshape(T, 6144)
+    nm = (T * 12288 + 255) // 256 * 256
+    kv = down16(ws[nb + nm: nb + nm + T * (cfg.hc + 1) * cfg.H * 2].view(torch.int16)).reshape(T, -1)
+    return dict(idx=idx, mem=mem, kv=kv, hidden=down16(h_d).reshape(T, cfg.hc, cfg.H),
+                gate=g_d.cpu().numpy().reshape(T, cfg.hc)), (wkv, wqk)
+
+
+def _check_forward(got, ref, hc, H):
+    assert np.array_equal(got["idx"], ref["idx"])
+    assert np.array_equal(got["mem"], ref["mem"])
+    assert_bf16_close(got["kv"], ref["kv"], what="kv")
+    T = got["hidden"].shape[0]
+    assert_bf16_close(got["hidden"].reshape(T * hc, H), ref["hidden"].reshape(T * hc, H), what="hidden")
+    well = np.abs(ref["dot"]) >= 1e-2
+    assert np.max(np.abs(got["gate"] - ref["gate"])[well]) <= 1e-3
+    return int((~well).sum())
+
+
+@pytest.mark.parametrize("dot_scale", [1.0, 1 / 16.0])
+def test_forward_tiny(E, dot_scale):
+    log(f"forward: tiny config, dot_scale={dot_scale}")
+    w = World.of("tiny")
+    cfg, p = w.cfg, w.params[0]
+    tok, cu = synth.token_batch(w.cfg)
+    hist = O.history_reset(1, p.pad_cid)
+    hidden = synth.hidden_bf16(cfg, 1, len(tok))
+    got, (wkv, wqk) = _run_forward(E, w, 0, tok, cu, hist, hidden, dot_scale)
+    ref = O.forward(tok, cu, hist, w.tmap, p, w.rows(0), wkv, wqk, hidden, cfg.H, cfg.hc,
+                    1e-6, dot_scale)
+    n_small = _check_forward(got, ref, cfg.hc, cfg.H)
+    log(f"  gates with |dot| < 1e-2 (excluded from the gate bar): {n_small}")
+
+
+def test_forward_is_deterministic(E):
+    w = World.of("tiny")
+    cfg, p = w.cfg, w.params[0]
+    tok, cu = synth.token_batch(w.cfg)
+    hist = O.history_reset(1, p.pad_cid)
+    hidden = synth.hidden_bf16(cfg, 1, len(tok))
+    a, _ = _run_forward(E, w, 0, tok, cu, hist, hidden)
+    b, _ = _run_forward(E, w, 0, tok, cu, hist, hidden)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_forward_decode_config(E):
+    """Decode-shaped: 64 sequences x 1 token, 16M-row table, 3-token history."""
+    log("forward: decode-shaped config (16M-row table on device)")
+    w = World.of("decode")
+    cfg, p = w.cfg, w.params[0]
+    ptok, pcu = synth.history_prefix_tokens(cfg)
+    hist_d = torch.empty(cfg.n_seqs * 3, dtype=torch.int32, device=DEV)
+    E.engram_history_reset(hist_d, p.pad_cid)
+    E.engram_history_append(hist_d, up32(ptok), up32(pcu), up32(w.tmap), p.pad_cid)
+    hist = O.history_append(O.history_reset(cfg.n_seqs, p.pad_cid), ptok, pcu, w.tmap, p.pad_cid)
+    assert np.array_equal(down32(hist_d).reshape(-1, 3), hist)
+    tok, cu = synth.token_batch(cfg)
+    hidden = synth.hidden_bf16(cfg, 1, len(tok))
+    got, (wkv, wqk) = _run_forward(E, w, 0, tok, cu, hist, hidden)
+    ref = O.forward(tok, cu, hist, w.tmap, p, w.rows(0), wkv, wqk, hidden, cfg.H, cfg.hc)
+    _check_forward(got, ref, cfg.hc, cfg.H)
