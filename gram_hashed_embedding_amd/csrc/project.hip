@@ -10,12 +10,21 @@
 // A dense contraction, so it runs on the matrix cores: gfx950
 // v_mfma_f32_32x32x16_bf16 with FP32 accumulation. Both operands are
 // K-contiguous, so every lane's MFMA fragment (8 consecutive K values of one
-// row) is one 16-byte LDS read. The workgroup tile is BM x BN x 64 with 4
-// waves in a 2 x 2 grid; tiles are double-buffered in LDS with one barrier
-// per K step. Workgroups are renumbered so that each XCD (which owns an L2)
-// receives a contiguous range of tiles, and tiles are visited in groups of
-// kGroupM row-tiles so concurrently running workgroups share both operands
-// in L2.
+// row) is one 16-byte LDS read. Workgroups are renumbered so that each XCD
+// (which owns an L2) receives a contiguous range of tiles, and tiles are
+// visited in groups of row-tiles so concurrently running workgroups share
+// both operands in L2.
+//
+// Two kernels:
+//  - project_kernel<BM, BN>: 4 waves in a 2 x 2 grid, register-staged loads
+//    into padded, double-buffered LDS, one barrier per K step. Used for small
+//    T, where few 256-row tiles would leave most CUs idle.
+//  - pingpong_kernel: 256 x 256 x 64 tiles, 8 waves. Global -> LDS loads go
+//    straight into LDS (global_load_lds_dwordx4) in an XOR-swizzled layout.
+//    The two waves that share a SIMD alternate roles every slot: one issues a
+//    cluster of 16 MFMAs while the other reads the next fragments from LDS
+//    and issues DMA for the next stage, so the matrix core stays busy while
+//    the other wave waits on memory.
 
 #include "engram_internal.h"
 
@@ -155,13 +164,207 @@ hipError_t run(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N, u
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- ping-pong kernel
+// Tile 256 x 256 x 64 (64 KB of LDS per stage, two stages), 512 threads.
+// Wave w (0..7) owns the 128 x 64 sub-tile (w / 4, w % 4); waves w and w + 4
+// share a SIMD. LDS rows are 128 bytes (64 bf16 of K); 16-byte chunk c of row
+// r is stored in slot c ^ swz(r), which keeps the 32-row fragment reads free
+// of bank conflicts. The DMA engine writes a wave's 64 x 16 bytes to one
+// contiguous kilobyte, so the swizzle is applied on the global side: the lane
+// that fills slot s of row r fetches chunk s ^ swz(r).
+//
+// Slots: group 0 (waves 0-3) runs Mem(kt,0) C(kt,0) Mem(kt,1) C(kt,1) for each
+// K step kt; group 1 (waves 4-7) runs the same clusters one slot later. Mem(kt,h)
+// reads the fragments of K-half h of stage kt (and, for h = 0, issues this
+// wave's DMA of stage kt+1 into the other buffer); C(kt,h) is 16 MFMAs. A
+// barrier ends every slot. Every wave waits for its own DMA of stage kt+1 in
+// slot 4kt+3, before the barrier after which stage kt+1 is first read.
+constexpr int kPPBM = 256, kPPBN = 256, kPPGroupM = 4;
+
+__device__ __forceinline__ int pp_swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+
+__device__ __forceinline__ void slot_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) const void* gptr_t;
+
+__global__ __launch_bounds__(512) void pingpong_kernel(const uint16_t* __restrict__ A,
+                                                       const uint16_t* __restrict__ B,
+                                                       uint16_t* __restrict__ C, int M, int N,
+                                                       int m_tiles, int n_tiles) {
+  constexpr int ROWB = 128;                               // bytes per LDS row (BK = 64)
+  constexpr int STAGE_A = kPPBM * ROWB, STAGE = (kPPBM + kPPBN) * ROWB;
+  constexpr int TM = 4, TN = 2;                           // 32 x 32 tiles per wave
+  constexpr int KT = K / BK;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+
+  const int total = m_tiles * n_tiles;
+  const int pid = blockIdx.x;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int xcd = pid % kXcds, lid = pid / kXcds;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + lid;
+  const int span = kPPGroupM * n_tiles;
+  const int first_m = (logical / span) * kPPGroupM;
+  const int gm = (m_tiles - first_m) < kPPGroupM ? (m_tiles - first_m) : kPPGroupM;
+  const int ing = logical % span;
+  const int m0 = (first_m + ing % gm) * kPPBM;
+  const int n0 = (ing / gm) * kPPBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wm = wave >> 2, wn = wave & 3;
+
+  // DMA sources, as byte offsets from the tile's first row (rows past the
+  // matrix edge re-read its last row; their results are never stored).
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (i * 8 + wave) * 64 + lane;
+    const int r = q >> 3, s = q & 7;
+    const int c = s ^ pp_swz(r);
+    const int ra = (m0 + r < M ? m0 + r : M - 1) - m0;
+    const int rb = (n0 + r < N ? n0 + r : N - 1) - n0;
+    offA[i] = (uint32_t)ra * (K * 2) + c * 16;
+    offB[i] = (uint32_t)rb * (K * 2) + c * 16;
+  }
+  const unsigned char* Ab = reinterpret_cast<const unsigned char*>(A) + (int64_t)m0 * (K * 2);
+  const unsigned char* Bb = reinterpret_cast<const unsigned char*>(B) + (int64_t)n0 * (K * 2);
+  auto dma = [&](int kt, int stage) {
+    unsigned char* sA = lds + stage * STAGE;
+    unsigned char* sB = sA + STAGE_A;
+    const unsigned char* a = Ab + kt * (BK * 2);
+    const unsigned char* b = Bb + kt * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(a + offA[i]), (lds_ptr_t)(sA + (i * 8 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(b + offB[i]), (lds_ptr_t)(sB + (i * 8 + wave) * 1024), 16, 0, 0);
+  };
+
+  // Fragment addresses: lane reads row (lane & 31) of its 32-row tile, chunk
+  // 2u + (lane >> 5) for K step u; XOR-ing u << 5 into the address selects u.
+  const int hi = lane >> 5;
+  uint32_t fa[TM], fb[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * 128 + i * 32 + (lane & 31);
+    fa[i] = r * ROWB + ((hi ^ pp_swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int r = wn * 64 + j * 32 + (lane & 31);
+    fb[j] = STAGE_A + r * ROWB + ((hi ^ pp_swz(r)) << 4);
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  bf16x8 fra[2][TM], frb[2][TN];
+
+  auto mem_cluster = [&](int kt, int h) {
+    if (h == 0 && kt + 1 < KT) dma(kt + 1, (kt + 1) & 1);
+    const unsigned char* st = lds + (kt & 1) * STAGE;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t x = (uint32_t)(2 * h + u) << 5;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fra[u][i] = *reinterpret_cast<const bf16x8*>(st + (fa[i] ^ x));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) frb[u][j] = *reinterpret_cast<const bf16x8*>(st + (fb[j] ^ x));
+    }
+  };
+  auto compute_cluster = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[u][i], frb[u][j], acc[i][j], 0, 0, 0);
+  };
+
+  dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  slot_barrier();
+  // Both groups execute 4*KT + 1 slot barriers; the branch is wave-uniform.
+  if (grp == 0) {
+    for (int kt = 0; kt < KT; ++kt) {
+      mem_cluster(kt, 0);
+      slot_barrier();
+      compute_cluster();
+      slot_barrier();
+      mem_cluster(kt, 1);
+      slot_barrier();
+      compute_cluster();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      slot_barrier();
+    }
+    slot_barrier();
+  } else {
+    slot_barrier();
+    for (int kt = 0; kt < KT; ++kt) {
+      mem_cluster(kt, 0);
+      slot_barrier();
+      compute_cluster();
+      slot_barrier();
+      mem_cluster(kt, 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      slot_barrier();
+      compute_cluster();
+      slot_barrier();
+    }
+  }
+
+  // Epilogue through LDS: bf16 tile [256][256], then 16-byte row stores.
+  uint16_t* sC = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+        sC[row * kPPBN + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+      }
+    }
+  __syncthreads();
+  for (int ch = tid; ch < kPPBM * (kPPBN / 8); ch += 512) {
+    const int row = ch >> 5, cc = ch & 31;
+    const int gr = m0 + row, gc = n0 + cc * 8;
+    if (gr < M && gc < N)
+      *reinterpret_cast<uint4*>(C + (int64_t)gr * N + gc) =
+          *reinterpret_cast<const uint4*>(sC + row * kPPBN + cc * 8);
+  }
+}
+
+hipError_t run_pingpong(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
+                        uint16_t* kv, hipStream_t st) {
+  const int m_tiles = (int)((T + kPPBM - 1) / kPPBM);
+  const int n_tiles = (N + kPPBN - 1) / kPPBN;
+  pingpong_kernel<<<m_tiles * n_tiles, 512, 0, st>>>(mem, wkv, kv, (int)T, N, m_tiles, n_tiles);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
                           uint16_t* kv, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (T <= 64) return run<64, 64>(mem, T, wkv, N, kv, st);
-  return run<128, 128>(mem, T, wkv, N, kv, st);
+  if (T < 1024) return run<128, 128>(mem, T, wkv, N, kv, st);
+  return run_pingpong(mem, T, wkv, N, kv, st);
 }
 
 }  // namespace engram

@@ -224,6 +224,46 @@ def test_project_ragged_n(E):
     assert_bf16_close(down16(kv).reshape(T, -1), O.project(mem, wkv), what="kv")
 
 
+@pytest.mark.parametrize("T", [1024, 1100, 2600])
+def test_project_large_t_tiny_width(E, T):
+    """T >= 1024 takes the 256 x 256 ping-pong kernel: several M tiles plus a ragged tail."""
+    log(f"project (256x256 tiles): tiny wkv, T={T}")
+    cfg = synth.CONFIGS["tiny"]
+    wkv = synth.wkv_bf16(cfg, 1)
+    rng = np.random.default_rng(T)
+    mem = synth.bf16_bits_from_f32(rng.standard_normal((T, 6144)).astype(np.float32) * 0.1)
+    kv = torch.empty(T * 1280, dtype=torch.int16, device=DEV)
+    E.engram_project(up16(mem), up16(wkv), cfg.H, cfg.hc, kv)
+    assert_bf16_close(down16(kv).reshape(T, -1), O.project(mem, wkv), what="kv")
+
+
+def test_project_large_t_ragged_n(E):
+    rng = np.random.default_rng(6)
+    H, hc, T = 64, 2, 1030
+    wkv = synth.bf16_bits_from_f32(0.02 * rng.standard_normal(((hc + 1) * H, 6144)).astype(np.float32))
+    mem = synth.bf16_bits_from_f32(rng.standard_normal((T, 6144)).astype(np.float32))
+    kv = torch.empty(T * (hc + 1) * H, dtype=torch.int16, device=DEV)
+    E.engram_project(up16(mem), up16(wkv), H, hc, kv)
+    assert_bf16_close(down16(kv).reshape(T, -1), O.project(mem, wkv), what="kv")
+
+
+def test_project_full_size_sampled_rows(E):
+    """4,096 tokens x full wkv (the full-size prefill shape): rows sampled at
+    tile edges and at random are compared with the oracle."""
+    log("project: 4,096 x 25,600 x 6,144, sampled rows")
+    cfg = synth.CONFIGS["full"]
+    T = 4096
+    wkv = synth.wkv_bf16(cfg, 1)
+    rng = np.random.default_rng(11)
+    mem = synth.bf16_bits_from_f32(rng.standard_normal((T, 6144)).astype(np.float32) * 0.1)
+    kv = torch.empty(T * 25600, dtype=torch.int16, device=DEV)
+    E.engram_project(up16(mem), up16(wkv), cfg.H, cfg.hc, kv)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 257, 2047, 2048, 4094, 4095],
+                                     rng.integers(0, T, 53)]))
+    got = down16(kv).reshape(T, -1)[rows]
+    assert_bf16_close(got, O.project(mem[rows], wkv), what="kv")
+
+
 @pytest.mark.parametrize("T", [64, 257])
 def test_project_full_width(E, T):
     log(f"project: full wkv 25,600 x 6,144, T={T}")
