@@ -9,18 +9,20 @@
 // spans, DEAD) are masked and pass through unchanged.
 //
 // HBM-bound: per token it reads hc branches of hidden and keys plus the value
-// and writes hidden back. One workgroup per token. Pass 1 forms the 3*hc
-// sums (sum h^2, sum k^2, sum h*k*w per branch) with 16-byte loads; they are
-// reduced across each wave with cross-lane moves, then across waves in LDS.
-// Pass 2 re-reads h and v (now in L2) and writes bf16(h + g*v).
+// (5 x 10 KB at H = 5,120) and writes hidden back. One workgroup per token,
+// one 16-byte chunk of 8 values per thread and branch (640 threads at
+// H = 5,120, which keeps registers low enough for two tokens per CU). Each
+// thread keeps its hidden and value chunks in registers, forms the 3*hc sums
+// (sum h^2, sum k^2, sum h*k*w per branch), reduces them across the wave with
+// cross-lane adds and across waves through LDS, then writes bf16(h + g*v)
+// from registers. Streamed data uses non-temporal accesses; the norm weights
+// (hc*H floats, shared by all tokens) stay in L2.
 
 #include "engram_internal.h"
 
 namespace engram {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kMaxHc = 8;
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -38,27 +40,132 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* f) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void gate_kernel(
+__device__ __forceinline__ float gate_of(float ss_h, float ss_k, float hkw, float inv_h, float eps,
+                                         float dot_scale) {
+  const float r_h = 1.0f / sqrtf(ss_h * inv_h + eps);
+  const float r_k = 1.0f / sqrtf(ss_k * inv_h + eps);
+  const float dot = dot_scale * r_h * r_k * hkw;
+  const float z = copysignf(sqrtf(fmaxf(fabsf(dot), 1e-6f)), dot);
+  return 1.0f / (1.0f + expf(-z));
+}
+
+// Reduce 3*HC per-thread sums to per-branch gates in g_sh (all threads read it after).
+template <int HC, int WAVES>
+__device__ __forceinline__ void reduce_gates(float (&s)[3 * HC], float* red, float* g_sh, int H,
+                                             float eps, float dot_scale, float* gate_out, int64_t t) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int q = 0; q < 3 * HC; ++q) {
+    const float v = wave_sum(s[q]);
+    if (lane == 0) red[q * WAVES + wave] = v;
+  }
+  __syncthreads();
+  if (tid < HC) {
+    float a = 0.f, k2 = 0.f, d = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      a += red[(3 * tid) * WAVES + w];
+      k2 += red[(3 * tid + 1) * WAVES + w];
+      d += red[(3 * tid + 2) * WAVES + w];
+    }
+    const float g = gate_of(a, k2, d, 1.0f / (float)H, eps, dot_scale);
+    g_sh[tid] = g;
+    if (gate_out != nullptr) gate_out[t * HC + tid] = g;
+  }
+  __syncthreads();
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte accesses: hidden and k/v are touched once.
+__device__ __forceinline__ uint4 nt_load(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store(uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
+                                         uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// Register-resident variant for H = 8 * THREADS: thread i owns chunk i of
+// every branch. Loads of hidden and value are issued first and stay in
+// registers; keys are streamed through the sums branch by branch.
+template <int HC, int THREADS>
+__global__ __launch_bounds__(THREADS) void gate_reg_kernel(
+    uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
+    const uint32_t* __restrict__ tok, float eps, float dot_scale, float* __restrict__ gate_out) {
+  constexpr int WAVES = THREADS / 64;
+  constexpr int H = THREADS * 8;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tok != nullptr && tok[t] == ENGRAM_DEAD_TOKEN) {
+    if (gate_out != nullptr && tid < HC) gate_out[t * HC + tid] = 0.0f;
+    return;
+  }
+  uint16_t* h_t = hidden + t * (int64_t)HC * H + tid * 8;
+  const uint16_t* kv_t = kv + t * (int64_t)(HC + 1) * H + tid * 8;
+  const uint4 vq = nt_load(kv_t + HC * H);
+  uint4 hq[HC];
+#pragma unroll
+  for (int b = 0; b < HC; ++b) hq[b] = nt_load(h_t + b * H);
+  float s[3 * HC];
+#pragma unroll
+  for (int b = 0; b < HC; ++b) {
+    const float4 w0 = *reinterpret_cast<const float4*>(wqk + b * H + tid * 8);
+    const float4 w1 = *reinterpret_cast<const float4*>(wqk + b * H + tid * 8 + 4);
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float h[8], k[8];
+    unpack8(hq[b], h);
+    unpack8(nt_load(kv_t + b * H), k);
+    s[3 * b] = s[3 * b + 1] = s[3 * b + 2] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[3 * b] = fmaf(h[i], h[i], s[3 * b]);
+      s[3 * b + 1] = fmaf(k[i], k[i], s[3 * b + 1]);
+      s[3 * b + 2] = fmaf(h[i] * k[i], w[i], s[3 * b + 2]);
+    }
+  }
+  __shared__ float red[3 * HC * WAVES];
+  __shared__ float g_sh[HC];
+  reduce_gates<HC, WAVES>(s, red, g_sh, H, eps, dot_scale, gate_out, t);
+  float v[8];
+  unpack8(vq, v);
+#pragma unroll
+  for (int b = 0; b < HC; ++b) {
+    const float g = g_sh[b];
+    float h[8];
+    unpack8(hq[b], h);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = f32_to_bf16_rne(fmaf(g, v[2 * i], h[2 * i])) |
+             (f32_to_bf16_rne(fmaf(g, v[2 * i + 1], h[2 * i + 1])) << 16);
+    nt_store(h_t + b * H, o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Generic variant (any H % 64 == 0, hc <= 8): 256 threads, strided chunks,
+// hidden and value re-read (from L2) for the residual.
+constexpr int kGenThreads = 256;
+__global__ __launch_bounds__(kGenThreads) void gate_generic_kernel(
     uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
     const uint32_t* __restrict__ tok, int H, int hc, float eps, float dot_scale,
     float* __restrict__ gate_out) {
+  constexpr int WAVES = kGenThreads / 64;
   const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool dead = tok != nullptr && tok[t] == ENGRAM_DEAD_TOKEN;
-  if (dead) {
+  const int tid = threadIdx.x;
+  if (tok != nullptr && tok[t] == ENGRAM_DEAD_TOKEN) {
     if (gate_out != nullptr && tid < hc) gate_out[t * hc + tid] = 0.0f;
     return;
   }
-  const int N = (hc + 1) * H;
   const int chunks = H / 8;
   uint16_t* h_t = hidden + t * (int64_t)hc * H;
-  const uint16_t* kv_t = kv + t * (int64_t)N;
-
-  float s_hh[kMaxHc], s_kk[kMaxHc], s_hk[kMaxHc];
+  const uint16_t* kv_t = kv + t * (int64_t)(hc + 1) * H;
+  float s[3 * kMaxHc];
 #pragma unroll
-  for (int b = 0; b < kMaxHc; ++b) s_hh[b] = s_kk[b] = s_hk[b] = 0.0f;
-
-  for (int c = tid; c < chunks; c += kThreads) {
+  for (int q = 0; q < 3 * kMaxHc; ++q) s[q] = 0.0f;
+  for (int c = tid; c < chunks; c += kGenThreads) {
 #pragma unroll
     for (int b = 0; b < kMaxHc; ++b) {
       if (b >= hc) break;
@@ -70,48 +177,37 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(
       const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        s_hh[b] = fmaf(h[i], h[i], s_hh[b]);
-        s_kk[b] = fmaf(k[i], k[i], s_kk[b]);
-        s_hk[b] = fmaf(h[i] * k[i], w[i], s_hk[b]);
+        s[3 * b] = fmaf(h[i], h[i], s[3 * b]);
+        s[3 * b + 1] = fmaf(k[i], k[i], s[3 * b + 1]);
+        s[3 * b + 2] = fmaf(h[i] * k[i], w[i], s[3 * b + 2]);
       }
     }
   }
-
-  __shared__ float red[3 * kMaxHc][kWaves];
+  __shared__ float red[3 * kMaxHc * WAVES];
   __shared__ float g_sh[kMaxHc];
+  const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int b = 0; b < kMaxHc; ++b) {
-    if (b >= hc) break;
-    const float a = wave_sum(s_hh[b]), k2 = wave_sum(s_kk[b]), d = wave_sum(s_hk[b]);
-    if (lane == 0) {
-      red[3 * b][wave] = a;
-      red[3 * b + 1][wave] = k2;
-      red[3 * b + 2][wave] = d;
-    }
+  for (int q = 0; q < 3 * kMaxHc; ++q) {
+    if (q >= 3 * hc) break;
+    const float v = wave_sum(s[q]);
+    if (lane == 0) red[q * WAVES + wave] = v;
   }
   __syncthreads();
   if (tid < hc) {
-    const int b = tid;
     float a = 0.f, k2 = 0.f, d = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      a += red[3 * b][w];
-      k2 += red[3 * b + 1][w];
-      d += red[3 * b + 2][w];
+    for (int w = 0; w < WAVES; ++w) {
+      a += red[(3 * tid) * WAVES + w];
+      k2 += red[(3 * tid + 1) * WAVES + w];
+      d += red[(3 * tid + 2) * WAVES + w];
     }
-    const float inv_h = 1.0f / (float)H;
-    const float r_h = 1.0f / sqrtf(a * inv_h + eps);
-    const float r_k = 1.0f / sqrtf(k2 * inv_h + eps);
-    const float dot = dot_scale * r_h * r_k * d;
-    const float z = copysignf(sqrtf(fmaxf(fabsf(dot), 1e-6f)), dot);
-    const float g = 1.0f / (1.0f + expf(-z));
-    g_sh[b] = g;
-    if (gate_out != nullptr) gate_out[t * hc + b] = g;
+    const float g = gate_of(a, k2, d, 1.0f / (float)H, eps, dot_scale);
+    g_sh[tid] = g;
+    if (gate_out != nullptr) gate_out[t * hc + tid] = g;
   }
   __syncthreads();
-
   const uint16_t* v_t = kv_t + (int64_t)hc * H;
-  for (int c = tid; c < chunks; c += kThreads) {
+  for (int c = tid; c < chunks; c += kGenThreads) {
     float v[8];
     unpack8(*reinterpret_cast<const uint4*>(v_t + c * 8), v);
 #pragma unroll
@@ -137,8 +233,13 @@ hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
                        const uint32_t* tok, int64_t T, int32_t H, int32_t hc, float eps,
                        float dot_scale, float* gate_out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  gate_kernel<<<(unsigned)T, kThreads, 0, st>>>(hidden, kv, wqk, tok, H, hc, eps, dot_scale,
-                                                gate_out);
+  if (hc == 4 && H == 5120) {
+    gate_reg_kernel<4, 640><<<(unsigned)T, 640, 0, st>>>(hidden, kv, wqk, tok, eps, dot_scale,
+                                                         gate_out);
+  } else {
+    gate_generic_kernel<<<(unsigned)T, kGenThreads, 0, st>>>(hidden, kv, wqk, tok, H, hc, eps,
+                                                             dot_scale, gate_out);
+  }
   return hipGetLastError();
 }
 

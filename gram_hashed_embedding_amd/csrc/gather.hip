@@ -22,38 +22,29 @@ constexpr int kBlock = 256;
 constexpr int kGroups = kBlock / 16;     // rows per pass of one workgroup
 constexpr int kRowsInFlight = 4;         // passes per workgroup (rows per lane)
 
-// Exact E4M3 x 2^(s-127) -> BF16 bits, rounded to nearest even where the
-// result falls below BF16's normal range. E4M3 is the OCP "FN" encoding
-// (bias 7, exponent 0 subnormal, S.1111.111 NaN, no infinity); E8M0 s = 255
-// is NaN. A NaN keeps the code's sign.
-__device__ __forceinline__ uint32_t mxfp8_to_bf16(uint32_t b, uint32_t s) {
-  const uint32_t sign = (b & 0x80u) << 8;
-  const uint32_t mag = b & 0x7Fu;
-  if (mag == 0x7Fu || s == 255u) return sign | 0x7FC0u;
-  if (mag == 0u) return sign;
-  const uint32_t e = mag >> 3, m = mag & 7u;
-  // value = M * 2^X, M = 1.mmm as an integer (normal) or 0.mmm (subnormal)
-  const int32_t M = e ? (int32_t)(8u | m) : (int32_t)m;
-  const int32_t X = (e ? (int32_t)e - 10 : -9) + (int32_t)s - 127;
-  const int32_t p = 31 - __builtin_clz((uint32_t)M);   // leading bit of M, 0..3
-  const int32_t E = X + p;                             // value in [2^E, 2^(E+1))
-  if (E > 127) return sign | 0x7F80u;                  // beyond BF16 range
-  if (E >= -126)
-    return sign | ((uint32_t)(E + 127) << 7) | (((uint32_t)M << (7 - p)) & 0x7Fu);
-  // BF16 subnormal: count quanta of 2^-133, ties to even.
-  const int32_t sh = X + 133;
-  if (sh >= 0) return sign | ((uint32_t)M << sh);
-  const int32_t r = -sh;
-  if (r > 4) return sign;                              // M < 16: below half a quantum
-  const uint32_t q = (uint32_t)M >> r;
-  const uint32_t rem = (uint32_t)M & ((1u << r) - 1u);
-  const uint32_t half = 1u << (r - 1);
-  return sign | (q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u));
+// Exact E4M3 x 2^(s-127) -> BF16, two codes at a time, on the gfx950
+// scaled-convert unit: v_cvt_scalef32_pk_bf16_fp8 multiplies each OCP E4M3
+// code by the power of two held in the exponent field of its float scale
+// operand (for a scale byte s that is the float with bits s << 23, so s = 0
+// and s = 255 need no special case) and rounds to BF16. Its results are exact
+// for every finite code and scale, BF16 subnormals included; every NaN it
+// produces is 0xFFC0. The method keeps each value's sign from its code, so
+// the sign bits are re-applied from the codes: a no-op for all non-NaN
+// results, and it turns NaNs into sign(code)|0x7FC0.
+template <bool HI>
+__device__ __forceinline__ uint32_t decode2(uint32_t w, float scale) {
+  const auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
+  const uint32_t bits = __builtin_bit_cast(uint32_t, r);
+  const uint32_t b = HI ? (w >> 16) : w;                      // the two codes in bytes 0, 1
+  const uint32_t signs = ((b << 8) & 0x8000u) | ((b << 16) & 0x80000000u);
+  return (bits & 0x7FFF7FFFu) | signs;
 }
 
-__device__ __forceinline__ uint32_t pack2(uint32_t w, int byte0, uint32_t s) {
-  return mxfp8_to_bf16((w >> (8 * byte0)) & 0xFFu, s) |
-         (mxfp8_to_bf16((w >> (8 * byte0 + 8)) & 0xFFu, s) << 16);
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void nt_store16(uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
+                                           uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
@@ -92,13 +83,15 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
     if (r >= total_rows) continue;
     uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
     if (live[u]) {
-      const uint32_t s = sc[u];
-      lo = make_uint4(pack2(c[u].x, 0, s), pack2(c[u].x, 2, s), pack2(c[u].y, 0, s), pack2(c[u].y, 2, s));
-      hi = make_uint4(pack2(c[u].z, 0, s), pack2(c[u].z, 2, s), pack2(c[u].w, 0, s), pack2(c[u].w, 2, s));
+      const float scale = __uint_as_float(sc[u] << 23);
+      lo = make_uint4(decode2<false>(c[u].x, scale), decode2<true>(c[u].x, scale),
+                      decode2<false>(c[u].y, scale), decode2<true>(c[u].y, scale));
+      hi = make_uint4(decode2<false>(c[u].z, scale), decode2<true>(c[u].z, scale),
+                      decode2<false>(c[u].w, scale), decode2<true>(c[u].w, scale));
     }
-    uint4* out = reinterpret_cast<uint4*>(mem + r * ENGRAM_ROW + lane16 * 16);
-    out[0] = lo;
-    out[1] = hi;
+    uint16_t* out = mem + r * ENGRAM_ROW + lane16 * 16;
+    nt_store16(out, lo.x, lo.y, lo.z, lo.w);
+    nt_store16(out + 8, hi.x, hi.y, hi.z, hi.w);
   }
 }
 
