@@ -349,6 +349,150 @@ __global__ __launch_bounds__(512) void pingpong_kernel(const uint16_t* __restric
   }
 }
 
+
+// ---------------------------------------------------------------- skinny kernel (T <= 256)
+// Decode-sized T: the projection streams the 315 MB of wkv once and is bound
+// by HBM, so the kernel is built to keep many wkv bytes in flight and to read
+// each wkv row in long contiguous runs.
+//
+// vmcnt retires loads in order, so a wave that mixed a deep HBM stream with
+// short L2 loads would drain the stream at every short wait; the work is
+// split between waves. In each workgroup wave 0 copies the mem rows (16*MT
+// padded rows) into an LDS ring of R stages with DMA; waves 1..NC each own 16
+// wkv rows and load them straight into registers as 16x16x32 MFMA B
+// fragments, U super-steps ahead. One barrier per super-step tells the
+// consumers that a mem stage has landed and the loader that the consumers
+// are done with the stage it refills.
+//
+// A super-step covers SK values of K (J = SK/32 MFMA K-steps). The K order
+// inside a super-step is permuted identically for both operands, which leaves
+// the sums unchanged: for K-step j, lane group g (lane >> 4) supplies chunk
+// g*J + j (8 values). So each lane reads SK/4 contiguous bytes of its row per
+// super-step and a wave asks for 16 rows x 2*SK contiguous bytes at once. In
+// LDS, chunk c of mem row r sits in slot c ^ (r & 7), which keeps the 16-row
+// fragment reads free of bank conflicts.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int MT, int NC, int R, int U, int SK>
+__global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* __restrict__ A,
+                                                               const uint16_t* __restrict__ B,
+                                                               uint16_t* __restrict__ C, int M,
+                                                               int N) {
+  constexpr int KS = K / SK;                 // super-steps
+  constexpr int J = SK / 32;                 // MFMA K-steps per super-step
+  constexpr int CH = SK / 8;                 // 16-byte chunks per row per super-step
+  constexpr int ROWS = MT * 16;
+  constexpr int ROWB = SK * 2;               // LDS bytes per mem row per stage
+  constexpr int STAGE = ROWS * ROWB;
+  constexpr int INSTR = STAGE / 1024;        // 1 KB DMA instructions per stage
+  static_assert(CH >= 8 && KS % U == 0 && KS > U, "super-step shape");
+  static_assert(R >= 2 && R <= 4 && (R - 2) * INSTR <= 63, "ring depth vs vmcnt range");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[R * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  if (wave == 0) {
+    // ---- mem loader
+    uint32_t off[INSTR];
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int q = i * 64 + lane, r = q / CH, sl = q % CH;
+      const int c = sl ^ (r & 7);
+      const int rr = r < M ? r : M - 1;
+      off[i] = (uint32_t)rr * (K * 2) + c * 16;
+    }
+    const unsigned char* Ab = reinterpret_cast<const unsigned char*>(A);
+    auto issue = [&](int ks) {
+      unsigned char* st = lds + (ks % R) * STAGE;
+#pragma unroll
+      for (int i = 0; i < INSTR; ++i)
+        __builtin_amdgcn_global_load_lds((gptr_t)(Ab + ks * ROWB + off[i]),
+                                         (lds_ptr_t)(st + i * 1024), 16, 0, 0);
+    };
+#pragma unroll
+    for (int ks = 0; ks < R - 1; ++ks) issue(ks);
+    for (int ks = 0; ks < KS; ++ks) {
+      // stages ks+1 .. ks+R-2 may stay in flight
+      const int newer = (KS - 1 - ks) < (R - 2) ? (KS - 1 - ks) : (R - 2);
+      if constexpr (R == 4) {
+        if (newer == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * INSTR) : "memory");
+        else if (newer == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INSTR) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else if constexpr (R == 3) {
+        if (newer == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(INSTR) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      slot_barrier();
+      if (ks + R - 1 < KS) issue(ks + R - 1);
+    }
+    return;
+  }
+
+  // ---- consumers
+  const int n0 = blockIdx.x * (16 * NC) + (wave - 1) * 16;
+  const int arow = lane & 15, g = lane >> 4;
+  int nr = n0 + arow;
+  nr = nr < N ? nr : N - 1;
+  const uint16_t* bp = B + (int64_t)nr * K + g * J * 8;   // this lane's SK/4-value span
+  bf16x8 bq[U][J];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int j = 0; j < J; ++j) bq[u][j] = *reinterpret_cast<const bf16x8*>(bp + u * SK + j * 8);
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](int ks, const bf16x8 (&b)[J]) {
+    slot_barrier();
+    const unsigned char* st = lds + (ks % R) * STAGE;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int r = i * 16 + arow;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * ROWB + (((g * J + j) ^ (r & 7)) << 4));
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i], 0, 0, 0);
+      }
+    }
+  };
+  // Steady state: consume super-step ks from ring slot u, refill it with ks + U.
+  for (int ks0 = 0; ks0 < KS - U; ks0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u;
+      step(ks, bq[u]);
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        bq[u][j] = *reinterpret_cast<const bf16x8*>(bp + (ks + U) * SK + j * 8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) step(KS - U + u, bq[u]);
+
+  // 16x16 accumulator layout: lane holds column lane & 15 and rows 4*(lane >> 4) + jj.
+  const int col = n0 + arow;
+  if (col < N) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int row = i * 16 + g * 4 + jj;
+        if (row < M) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][jj]);
+      }
+  }
+}
+
+template <int MT, int NC, int R, int U, int SK>
+hipError_t run_skinny(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N, uint16_t* kv,
+                      hipStream_t st) {
+  const int blocks = (N + 16 * NC - 1) / (16 * NC);
+  skinny_kernel<MT, NC, R, U, SK><<<blocks, 64 * (NC + 1), 0, st>>>(mem, wkv, kv, (int)T, N);
+  return hipGetLastError();
+}
+
 hipError_t run_pingpong(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
                         uint16_t* kv, hipStream_t st) {
   const int m_tiles = (int)((T + kPPBM - 1) / kPPBM);
@@ -362,7 +506,12 @@ hipError_t run_pingpong(const uint16_t* mem, int64_t T, const uint16_t* wkv, int
 hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
                           uint16_t* kv, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (T <= 64) return run<64, 64>(mem, T, wkv, N, kv, st);
+  // <MT, NC, R, U, SK> chosen by a sweep on the 25,600 x 6,144 wkv stream
+  if (T <= 16) return run_skinny<1, 4, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 32) return run_skinny<2, 4, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 64) return run_skinny<4, 8, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 128) return run_skinny<8, 4, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 256) return run_skinny<16, 4, 2, 4, 64>(mem, T, wkv, N, kv, st);
   if (T < 1024) return run<128, 128>(mem, T, wkv, N, kv, st);
   return run_pingpong(mem, T, wkv, N, kv, st);
 }
