@@ -86,3 +86,48 @@ def device_table(E, n_rows: int, key_data: int, key_scale: int):
     scales = torch.empty(n_rows * 8, dtype=torch.uint8, device=DEV)
     E.engram_gen_table(codes, scales, 0, n_rows, key_data, key_scale)
     return codes, scales
+
+
+def hidden_device(cfg, layer: int, T: int, first: int = 0, batch: int = 0) -> torch.Tensor:
+    """Seeded hidden rows [first, first+T) generated chunk-parallel on the host
+    and uploaded as int16 [T][hc][H]."""
+    import concurrent.futures as cf
+    out = torch.empty((T, cfg.hc, cfg.H), dtype=torch.int16, device=DEV)
+    C = synth.HIDDEN_CHUNK
+    # chunk-aligned pieces
+    pieces, a = [], first
+    while a < first + T:
+        b = min(first + T, (a // C + 1) * C)
+        pieces.append((a, b))
+        a = b
+
+    def gen(ab):
+        a, b = ab
+        return a, synth.hidden_bf16(cfg, layer, b - a, batch=batch, first=a)
+
+    with cf.ThreadPoolExecutor(max_workers=16) as ex:
+        for a, h in ex.map(gen, pieces):
+            out[a - first:a - first + h.shape[0]].copy_(torch.from_numpy(h.view(np.int16)))
+    return out
+
+
+def hidden_rows(cfg, layer: int, rows, batch: int = 0) -> np.ndarray:
+    """Seeded hidden for selected global token rows (regenerating whole chunks once)."""
+    rows = np.asarray(rows)
+    out = np.empty((len(rows), cfg.hc, cfg.H), dtype=np.uint16)
+    C = synth.HIDDEN_CHUNK
+    for c in np.unique(rows // C):
+        chunk = synth.hidden_bf16(cfg, layer, C, batch=batch, first=int(c) * C)
+        sel = rows // C == c
+        out[sel] = chunk[rows[sel] - int(c) * C]
+    return out
+
+
+def workspace_views(ws: torch.Tensor, T: int, H: int, hc: int):
+    """(idx [T][24], mem [T][6144], kv [T][(hc+1)H]) host copies of engram_forward's workspace."""
+    r = lambda x: (x + 255) // 256 * 256
+    nb, nm = r(T * 96), r(T * 12288)
+    idx = ws[: T * 96].view(torch.int32)
+    mem = ws[nb: nb + T * 12288].view(torch.int16)
+    kv = ws[nb + nm: nb + nm + T * (hc + 1) * H * 2].view(torch.int16)
+    return idx, mem, kv
