@@ -19,12 +19,9 @@
 //  - project_kernel<BM, BN>: 4 waves in a 2 x 2 grid, register-staged loads
 //    into padded, double-buffered LDS, one barrier per K step. Used for small
 //    T, where few 256-row tiles would leave most CUs idle.
-//  - pingpong_kernel: 256 x 256 x 64 tiles, 8 waves. Global -> LDS loads go
-//    straight into LDS (global_load_lds_dwordx4) in an XOR-swizzled layout.
-//    The two waves that share a SIMD alternate roles every slot: one issues a
-//    cluster of 16 MFMAs while the other reads the next fragments from LDS
-//    and issues DMA for the next stage, so the matrix core stays busy while
-//    the other wave waits on memory.
+//  - wave_tile_kernel: 256 x 256 x 64 tiles, 4 waves of 128 x 128 each, loads
+//    staged through registers two K steps ahead and spread between the MFMAs.
+//  - skinny_kernel: decode-sized T, where the projection is a stream of wkv.
 
 #include "engram_internal.h"
 
@@ -165,25 +162,221 @@ hipError_t run(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N, u
 }
 
 
-// ---------------------------------------------------------------- ping-pong kernel
-// Tile 256 x 256 x 64 (64 KB of LDS per stage, two stages), 512 threads.
-// Wave w (0..7) owns the 128 x 64 sub-tile (w / 4, w % 4); waves w and w + 4
-// share a SIMD. LDS rows are 128 bytes (64 bf16 of K); 16-byte chunk c of row
-// r is stored in slot c ^ swz(r), which keeps the 32-row fragment reads free
-// of bank conflicts. The DMA engine writes a wave's 64 x 16 bytes to one
-// contiguous kilobyte, so the swizzle is applied on the global side: the lane
-// that fills slot s of row r fetches chunk s ^ swz(r).
+// ---------------------------------------------------------------- wave-tile kernel
+// Tile 256 x 256 x 64, 4 waves (one per SIMD), each owning a 128 x 128
+// sub-tile: 16 accumulators of 32 x 32 fill the 256 accumulation registers,
+// and every K16 step issues 16 MFMAs against 8 fragment reads, the lowest LDS
+// traffic per MFMA a wave can have.
 //
-// Slots: group 0 (waves 0-3) runs Mem(kt,0) C(kt,0) Mem(kt,1) C(kt,1) for each
-// K step kt; group 1 (waves 4-7) runs the same clusters one slot later. Mem(kt,h)
-// reads the fragments of K-half h of stage kt (and, for h = 0, issues this
-// wave's DMA of stage kt+1 into the other buffer); C(kt,h) is 16 MFMAs. A
-// barrier ends every slot. Every wave waits for its own DMA of stage kt+1 in
-// slot 4kt+3, before the barrier after which stage kt+1 is first read.
-constexpr int kPPBM = 256, kPPBN = 256, kPPGroupM = 4;
+// Operands are staged through registers, two K steps ahead: in K step kt a
+// thread writes its chunks of tile kt+1 from register set (kt+1) % 2 into the
+// idle LDS buffer and then reloads that set with tile kt+3, so a global load
+// has two whole K steps (~4,000 cycles) to return. Loads use buffer
+// instructions whose row offsets sit in per-chunk registers and whose K
+// position is a scalar offset. Each K step is cut into four K16 steps; the
+// loads, LDS writes and next fragment reads are spread between the MFMAs of
+// the first three, and one barrier, before the last, publishes tile kt+1.
+//
+// LDS rows are 128 bytes (64 bf16 of K); 16-byte chunk c of row r is stored
+// in slot c ^ swz(r), which keeps the 32-row fragment reads free of bank
+// conflicts. The MFMA takes the wkv fragment as its first operand, so an
+// accumulator holds a 32 x 32 block of kv transposed: each lane ends with
+// four consecutive kv columns of one row, stored to LDS as one 8-byte write
+// and then written out in 16-byte row chunks.
+constexpr int kWTBM = 256, kWTBN = 256, kWTGroupM = 8;
 
-__device__ __forceinline__ int pp_swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+__device__ __forceinline__ int wt_swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Order inside one K16 step: 16 MFMAs with NW LDS writes, NV global loads
+// and NR fragment reads placed between them; nothing crosses the step.
+template <int NW, int NV, int NR>
+__device__ __forceinline__ void wt_interleave() {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+    if (q < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // DS write
+    if (q >= 2 && q - 2 < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+    if (q >= 16 - NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void wave_tile_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B,
+                                                        uint16_t* __restrict__ C, int M, int N,
+                                                        int m_tiles, int n_tiles) {
+  constexpr int BM = kWTBM, BN = kWTBN, ROWB = 128;
+  constexpr int STAGE_A = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int TM = 4, TN = 4;
+  constexpr int KT = K / BK;
+  static_assert(KT % 2 == 0, "K steps come in pairs");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+
+  const int total = m_tiles * n_tiles;
+  const int pid = blockIdx.x;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int xcd = pid % kXcds, lid = pid / kXcds;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + lid;
+  const int span = kWTGroupM * n_tiles;
+  const int first_m = (logical / span) * kWTGroupM;
+  const int gm = (m_tiles - first_m) < kWTGroupM ? (m_tiles - first_m) : kWTGroupM;
+  const int ing = logical % span;
+  const int m0 = (first_m + ing % gm) * BM;
+  const int n0 = (ing / gm) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Staging: thread t owns chunks (row (t >> 3) + 32 i, chunk t & 7), i < 8,
+  // of both operands; swz(row) does not depend on i. Rows past the edge of A
+  // or B re-read its last row (their products are never stored), so every
+  // address stays inside the operands.
+  const int rowsA = (M - m0) < BM ? (M - m0) : BM;
+  const int rowsB = (N - n0) < BN ? (N - n0) : BN;
+  const auto rsA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A) + (int64_t)m0 * K, 0,
+                                                    rowsA * K * 2, 0x00020000);
+  const auto rsB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B) + (int64_t)n0 * K, 0,
+                                                    rowsB * K * 2, 0x00020000);
+  const int gr = tid >> 3, gc = tid & 7;
+  int voffA[8], voffB[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = gr + 32 * i;
+    voffA[i] = (r < rowsA ? r : rowsA - 1) * (K * 2) + gc * 16;
+    voffB[i] = (r < rowsB ? r : rowsB - 1) * (K * 2) + gc * 16;
+  }
+  const uint32_t soff0 = gr * ROWB + ((gc ^ wt_swz(gr)) << 4);
+
+  i32x4 ra[2][8], rb[2][8];
+  auto gload = [&](int set, int kt, int i0, int cnt) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < i0 || i >= i0 + cnt) continue;
+      ra[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, voffA[i], kt * (BK * 2), 0);
+      rb[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsB, voffB[i], kt * (BK * 2), 0);
+    }
+  };
+  auto swrite = [&](int set, int buf, int i0, int cnt) {
+    unsigned char* st = lds + buf * STAGE + soff0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < i0 || i >= i0 + cnt) continue;
+      *reinterpret_cast<i32x4*>(st + i * 4096) = ra[set][i];
+      *reinterpret_cast<i32x4*>(st + STAGE_A + i * 4096) = rb[set][i];
+    }
+  };
+
+  // Fragments: lane reads row (lane & 31) of a 32-row block, chunk 2u + (lane >> 5)
+  // for K16 step u; swz depends on row bits 0..3 only, so the blocks are 4 KB
+  // apart and u flips bits 5-6 of the address.
+  const int hi = lane >> 5;
+  const int fra0 = wm * 128 + (lane & 31), frb0 = wn * 128 + (lane & 31);
+  const uint32_t fa0 = fra0 * ROWB + ((hi ^ wt_swz(fra0)) << 4);
+  const uint32_t fb0 = STAGE_A + frb0 * ROWB + ((hi ^ wt_swz(frb0)) << 4);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+  bf16x8 fa[2][TM], fb[2][TN];
+  auto load_frags = [&](int buf, int u, int fbuf) {
+    const unsigned char* st = lds + buf * STAGE;
+    const uint32_t x = (uint32_t)u << 5;
+    const unsigned char* pa = st + (fa0 ^ x);
+    const unsigned char* pb = st + (fb0 ^ x);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[fbuf][i] = *reinterpret_cast<const bf16x8*>(pa + i * 4096);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[fbuf][j] = *reinterpret_cast<const bf16x8*>(pb + j * 4096);
+  };
+  auto mfmas = [&](int fbuf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fbuf][j], fa[fbuf][i], acc[i][j], 0, 0, 0);
+  };
+
+  // Prologue: tile 0 into LDS buffer 0, tiles 1 and 2 into register sets 1 and 0.
+  gload(0, 0, 0, 8);
+  swrite(0, 0, 0, 8);
+  gload(1, 1, 0, 8);
+  gload(0, 2, 0, 8);
+  lds_barrier();
+  load_frags(0, 0, 0);
+
+  // K step kt (LDS buffer kt & 1, register set (kt+1) & 1; the set is a
+  // compile-time index, hence the loop over pairs of steps).
+#define WT_K16(SET, U, I0, CNT)                          \
+  mfmas((U) & 1);                                        \
+  load_frags(cur, (U) + 1, ((U) + 1) & 1);               \
+  swrite(SET, nxt, I0, CNT);                             \
+  gload(SET, ktn, I0, CNT);                              \
+  wt_interleave<2 * (CNT), 2 * (CNT), 8>();
+#define WT_KSTEP(KTV, SET)                                        \
+  {                                                               \
+    const int cur = (KTV) & 1, nxt = cur ^ 1;                     \
+    const int ktn = (KTV) + 3 < KT ? (KTV) + 3 : KT - 1;          \
+    WT_K16(SET, 0, 0, 3)                                          \
+    WT_K16(SET, 1, 3, 3)                                          \
+    WT_K16(SET, 2, 6, 2)                                          \
+    lds_barrier();                                                \
+    mfmas(1);                                                     \
+    load_frags(nxt, 0, 0);                                        \
+    wt_interleave<0, 0, 8>();                                     \
+  }
+  for (int kt = 0; kt < KT; kt += 2) {
+    WT_KSTEP(kt, 1)
+    WT_KSTEP(kt + 1, 0)
+  }
+#undef WT_KSTEP
+#undef WT_K16
+
+  // Epilogue. The accumulators are read with explicit v_accvgpr_read (which
+  // keeps the compiler from copying them out of the accumulation registers
+  // inside the loop); the nops cover the last MFMAs' result latency.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __syncthreads();
+  // kv tile in LDS: [256 rows][512 bytes], 16-byte chunk c of row r at c ^ (r & 15).
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int row = wm * 128 + i * 32 + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[i][j][4 * g + e]));
+        const uint32_t w0 = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t w1 = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        const int chunk = (wn * 16 + j * 4 + g) ^ (row & 15);
+        *reinterpret_cast<uint2*>(lds + row * 512 + chunk * 16 + hi * 8) = make_uint2(w0, w1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  __syncthreads();
+  for (int ch = tid; ch < BM * 32; ch += 256) {
+    const int row = ch >> 5, cc = ch & 31;
+    const int grow = m0 + row, gcol = n0 + cc * 8;
+    if (grow < M && gcol < N)
+      *reinterpret_cast<uint4*>(C + (int64_t)grow * N + gcol) =
+          *reinterpret_cast<const uint4*>(lds + row * 512 + ((cc ^ (row & 15)) << 4));
+  }
+}
+
+// Shared by the skinny kernel below.
 __device__ __forceinline__ void slot_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
@@ -192,162 +385,6 @@ __device__ __forceinline__ void slot_barrier() {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) const void* gptr_t;
-
-__global__ __launch_bounds__(512) void pingpong_kernel(const uint16_t* __restrict__ A,
-                                                       const uint16_t* __restrict__ B,
-                                                       uint16_t* __restrict__ C, int M, int N,
-                                                       int m_tiles, int n_tiles) {
-  constexpr int ROWB = 128;                               // bytes per LDS row (BK = 64)
-  constexpr int STAGE_A = kPPBM * ROWB, STAGE = (kPPBM + kPPBN) * ROWB;
-  constexpr int TM = 4, TN = 2;                           // 32 x 32 tiles per wave
-  constexpr int KT = K / BK;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
-
-  const int total = m_tiles * n_tiles;
-  const int pid = blockIdx.x;
-  const int per = total / kXcds, rem = total % kXcds;
-  const int xcd = pid % kXcds, lid = pid / kXcds;
-  const int logical = xcd * per + (xcd < rem ? xcd : rem) + lid;
-  const int span = kPPGroupM * n_tiles;
-  const int first_m = (logical / span) * kPPGroupM;
-  const int gm = (m_tiles - first_m) < kPPGroupM ? (m_tiles - first_m) : kPPGroupM;
-  const int ing = logical % span;
-  const int m0 = (first_m + ing % gm) * kPPBM;
-  const int n0 = (ing / gm) * kPPBN;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int wm = wave >> 2, wn = wave & 3;
-
-  // DMA sources, as byte offsets from the tile's first row (rows past the
-  // matrix edge re-read its last row; their results are never stored).
-  uint32_t offA[4], offB[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = (i * 8 + wave) * 64 + lane;
-    const int r = q >> 3, s = q & 7;
-    const int c = s ^ pp_swz(r);
-    const int ra = (m0 + r < M ? m0 + r : M - 1) - m0;
-    const int rb = (n0 + r < N ? n0 + r : N - 1) - n0;
-    offA[i] = (uint32_t)ra * (K * 2) + c * 16;
-    offB[i] = (uint32_t)rb * (K * 2) + c * 16;
-  }
-  const unsigned char* Ab = reinterpret_cast<const unsigned char*>(A) + (int64_t)m0 * (K * 2);
-  const unsigned char* Bb = reinterpret_cast<const unsigned char*>(B) + (int64_t)n0 * (K * 2);
-  auto dma = [&](int kt, int stage) {
-    unsigned char* sA = lds + stage * STAGE;
-    unsigned char* sB = sA + STAGE_A;
-    const unsigned char* a = Ab + kt * (BK * 2);
-    const unsigned char* b = Bb + kt * (BK * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(a + offA[i]), (lds_ptr_t)(sA + (i * 8 + wave) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(b + offB[i]), (lds_ptr_t)(sB + (i * 8 + wave) * 1024), 16, 0, 0);
-  };
-
-  // Fragment addresses: lane reads row (lane & 31) of its 32-row tile, chunk
-  // 2u + (lane >> 5) for K step u; XOR-ing u << 5 into the address selects u.
-  const int hi = lane >> 5;
-  uint32_t fa[TM], fb[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = wm * 128 + i * 32 + (lane & 31);
-    fa[i] = r * ROWB + ((hi ^ pp_swz(r)) << 4);
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int r = wn * 64 + j * 32 + (lane & 31);
-    fb[j] = STAGE_A + r * ROWB + ((hi ^ pp_swz(r)) << 4);
-  }
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  bf16x8 fra[2][TM], frb[2][TN];
-
-  auto mem_cluster = [&](int kt, int h) {
-    if (h == 0 && kt + 1 < KT) dma(kt + 1, (kt + 1) & 1);
-    const unsigned char* st = lds + (kt & 1) * STAGE;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t x = (uint32_t)(2 * h + u) << 5;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fra[u][i] = *reinterpret_cast<const bf16x8*>(st + (fa[i] ^ x));
-#pragma unroll
-      for (int j = 0; j < TN; ++j) frb[u][j] = *reinterpret_cast<const bf16x8*>(st + (fb[j] ^ x));
-    }
-  };
-  auto compute_cluster = [&]() {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fra[u][i], frb[u][j], acc[i][j], 0, 0, 0);
-  };
-
-  dma(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  slot_barrier();
-  // Both groups execute 4*KT + 1 slot barriers; the branch is wave-uniform.
-  if (grp == 0) {
-    for (int kt = 0; kt < KT; ++kt) {
-      mem_cluster(kt, 0);
-      slot_barrier();
-      compute_cluster();
-      slot_barrier();
-      mem_cluster(kt, 1);
-      slot_barrier();
-      compute_cluster();
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      slot_barrier();
-    }
-    slot_barrier();
-  } else {
-    slot_barrier();
-    for (int kt = 0; kt < KT; ++kt) {
-      mem_cluster(kt, 0);
-      slot_barrier();
-      compute_cluster();
-      slot_barrier();
-      mem_cluster(kt, 1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      slot_barrier();
-      compute_cluster();
-      slot_barrier();
-    }
-  }
-
-  // Epilogue through LDS: bf16 tile [256][256], then 16-byte row stores.
-  uint16_t* sC = reinterpret_cast<uint16_t*>(lds);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-        sC[row * kPPBN + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-      }
-    }
-  __syncthreads();
-  for (int ch = tid; ch < kPPBM * (kPPBN / 8); ch += 512) {
-    const int row = ch >> 5, cc = ch & 31;
-    const int gr = m0 + row, gc = n0 + cc * 8;
-    if (gr < M && gc < N)
-      *reinterpret_cast<uint4*>(C + (int64_t)gr * N + gc) =
-          *reinterpret_cast<const uint4*>(sC + row * kPPBN + cc * 8);
-  }
-}
 
 
 // ---------------------------------------------------------------- skinny kernel (T <= 256)
@@ -493,11 +530,11 @@ hipError_t run_skinny(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32
   return hipGetLastError();
 }
 
-hipError_t run_pingpong(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
-                        uint16_t* kv, hipStream_t st) {
-  const int m_tiles = (int)((T + kPPBM - 1) / kPPBM);
-  const int n_tiles = (N + kPPBN - 1) / kPPBN;
-  pingpong_kernel<<<m_tiles * n_tiles, 512, 0, st>>>(mem, wkv, kv, (int)T, N, m_tiles, n_tiles);
+hipError_t run_wave_tile(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
+                         uint16_t* kv, hipStream_t st) {
+  const int m_tiles = (int)((T + kWTBM - 1) / kWTBM);
+  const int n_tiles = (N + kWTBN - 1) / kWTBN;
+  wave_tile_kernel<<<m_tiles * n_tiles, 256, 0, st>>>(mem, wkv, kv, (int)T, N, m_tiles, n_tiles);
   return hipGetLastError();
 }
 
@@ -513,7 +550,7 @@ hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, i
   if (T <= 128) return run_skinny<8, 4, 4, 8, 64>(mem, T, wkv, N, kv, st);
   if (T <= 256) return run_skinny<16, 4, 2, 4, 64>(mem, T, wkv, N, kv, st);
   if (T < 1024) return run<128, 128>(mem, T, wkv, N, kv, st);
-  return run_pingpong(mem, T, wkv, N, kv, st);
+  return run_wave_tile(mem, T, wkv, N, kv, st);
 }
 
 }  // namespace engram

@@ -226,7 +226,7 @@ def test_project_ragged_n(E):
 
 @pytest.mark.parametrize("T", [1024, 1100, 2600])
 def test_project_large_t_tiny_width(E, T):
-    """T >= 1024 takes the 256 x 256 ping-pong kernel: several M tiles plus a ragged tail."""
+    """T >= 1024 takes the 256 x 256 wave-tile kernel: several M tiles plus a ragged tail."""
     log(f"project (256x256 tiles): tiny wkv, T={T}")
     cfg = synth.CONFIGS["tiny"]
     wkv = synth.wkv_bf16(cfg, 1)
