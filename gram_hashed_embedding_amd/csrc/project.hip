@@ -193,16 +193,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Order inside one K16 step: 16 MFMAs with NW LDS writes, NV global loads
-// and NR fragment reads placed between them; nothing crosses the step.
+// Order inside one K16 step: 16 MFMAs with the LDS writes on the even MFMA
+// slots, the global loads on the odd ones and the NR fragment reads in the
+// back half; nothing crosses the step. Spacing the 16-byte LDS writes keeps
+// the LDS write-data queue from filling, which would stall MFMA issue.
 template <int NW, int NV, int NR>
 __device__ __forceinline__ void wt_interleave() {
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-    if (q < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // DS write
-    if (q >= 2 && q - 2 < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-    if (q >= 16 - NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               // MFMA
+    if ((q & 1) == 0 && q / 2 < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
+    if ((q & 1) == 1 && q / 2 < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+    if (q >= 16 - NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // DS read
   }
   __builtin_amdgcn_sched_barrier(0);
 }
