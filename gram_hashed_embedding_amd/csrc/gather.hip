@@ -7,11 +7,13 @@
 // [vLLM] How it works: the fetched rows are concatenated into one memory
 // vector per position (bucket j fills values j*256 .. j*256+255).
 //
-// HBM-bound. A 16-lane group owns one 256-byte row: each lane loads 16
-// codes with one 16-byte load plus the byte of the scale its codes share
-// (lanes 2q and 2q+1 share scale q), decodes, and writes 32 bytes. Each lane
-// keeps kRowsInFlight rows' loads outstanding before decoding to cover the
-// latency of random HBM reads.
+// HBM-bound. A 16-lane group owns one 256-byte row: lane l loads the 8 codes
+// at l*8 and the 8 at 128 + l*8 (two 8-byte loads) plus the row's 8 scale
+// bytes, decodes, and writes 16 bytes to each half of the 512-byte BF16 row,
+// so every store instruction covers whole contiguous lines (stores of
+// 16 bytes at a 32-byte stride left partial lines and cost 16% more time).
+// Each lane keeps kRowsInFlight rows' loads outstanding before decoding to
+// cover the latency of random HBM reads.
 
 #include "engram_internal.h"
 
@@ -51,26 +53,33 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
     const uint32_t* __restrict__ idx, int64_t total_rows, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, uint64_t n_rows, uint16_t* __restrict__ mem,
     uint32_t* err) {
-  const int lane16 = threadIdx.x & 15;
+  const int l = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;
   const int64_t base = (int64_t)blockIdx.x * (kGroups * kRowsInFlight);
 
-  uint4 c[kRowsInFlight];
-  uint32_t sc[kRowsInFlight];
+  // Codes [8l, 8l+8) use scale l/4 (byte l/4 of the first scale word) and
+  // codes [128+8l, 128+8l+8) use scale 4 + l/4 (same byte of the second).
+  const int sh = 8 * (l >> 2);
+  uint2 ca[kRowsInFlight], cb[kRowsInFlight];
+  uint32_t sa[kRowsInFlight], sb[kRowsInFlight];
   bool live[kRowsInFlight];
 #pragma unroll
   for (int u = 0; u < kRowsInFlight; ++u) {
     const int64_t r = base + u * kGroups + grp;
     live[u] = false;
-    c[u] = make_uint4(0, 0, 0, 0);
-    sc[u] = 127;
+    ca[u] = cb[u] = make_uint2(0, 0);
+    sa[u] = sb[u] = 127;
     if (r < total_rows) {
       const uint32_t row = idx[r];
       if (row != ENGRAM_DEAD_IDX) {
         if ((uint64_t)row < n_rows) {
           live[u] = true;
-          c[u] = *reinterpret_cast<const uint4*>(codes + (uint64_t)row * ENGRAM_ROW + lane16 * 16);
-          sc[u] = scales[(uint64_t)row * ENGRAM_SCALES_PER_ROW + (lane16 >> 1)];
+          const uint8_t* cr = codes + (uint64_t)row * ENGRAM_ROW;
+          ca[u] = *reinterpret_cast<const uint2*>(cr + l * 8);
+          cb[u] = *reinterpret_cast<const uint2*>(cr + 128 + l * 8);
+          const uint2 s2 = *reinterpret_cast<const uint2*>(scales + (uint64_t)row * ENGRAM_SCALES_PER_ROW);
+          sa[u] = (s2.x >> sh) & 0xFFu;
+          sb[u] = (s2.y >> sh) & 0xFFu;
         } else {
           set_err(err, ENGRAM_ERR_ROW_RANGE);
         }
@@ -81,17 +90,17 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
   for (int u = 0; u < kRowsInFlight; ++u) {
     const int64_t r = base + u * kGroups + grp;
     if (r >= total_rows) continue;
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
     if (live[u]) {
-      const float scale = __uint_as_float(sc[u] << 23);
-      lo = make_uint4(decode2<false>(c[u].x, scale), decode2<true>(c[u].x, scale),
-                      decode2<false>(c[u].y, scale), decode2<true>(c[u].y, scale));
-      hi = make_uint4(decode2<false>(c[u].z, scale), decode2<true>(c[u].z, scale),
-                      decode2<false>(c[u].w, scale), decode2<true>(c[u].w, scale));
+      const float s0 = __uint_as_float(sa[u] << 23), s1 = __uint_as_float(sb[u] << 23);
+      a = make_uint4(decode2<false>(ca[u].x, s0), decode2<true>(ca[u].x, s0),
+                     decode2<false>(ca[u].y, s0), decode2<true>(ca[u].y, s0));
+      b = make_uint4(decode2<false>(cb[u].x, s1), decode2<true>(cb[u].x, s1),
+                     decode2<false>(cb[u].y, s1), decode2<true>(cb[u].y, s1));
     }
-    uint16_t* out = mem + r * ENGRAM_ROW + lane16 * 16;
-    nt_store16(out, lo.x, lo.y, lo.z, lo.w);
-    nt_store16(out + 8, hi.x, hi.y, hi.z, hi.w);
+    uint16_t* out = mem + r * ENGRAM_ROW;
+    nt_store16(out + l * 8, a.x, a.y, a.z, a.w);
+    nt_store16(out + 128 + l * 8, b.x, b.y, b.z, b.w);
   }
 }
 
