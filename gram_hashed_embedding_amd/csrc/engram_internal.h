@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/engram.h"
 
 namespace engram {
@@ -31,6 +33,30 @@ hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
 hipError_t launch_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin,
                             uint64_t n_rows, uint64_t key_data, uint64_t key_scale,
                             hipStream_t st);
+
+// Compute units of the current device, looked up once per device (kernels
+// that keep one workgroup per CU size their grids with it).
+inline hipError_t cu_count(int* n) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *n = c;
+      return hipSuccess;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (c < 1) c = 1;
+  if (cached) cache[dev].store(c, std::memory_order_relaxed);
+  *n = c;
+  return hipSuccess;
+}
 
 // ---------------------------------------------------------------- device helpers
 // float32 -> bfloat16 bits, round to nearest even (gfx950 converts in hardware).

@@ -18,37 +18,12 @@
 // already in flight. Streamed data uses non-temporal accesses; the norm
 // weights (hc*H floats, shared by all tokens) stay in L2.
 
-#include <atomic>
-
 #include "engram_internal.h"
 
 namespace engram {
 namespace {
 
 constexpr int kMaxHc = 8;
-
-// Compute units of the current device, looked up once per device.
-hipError_t cu_count(int* n) {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const bool cached = dev >= 0 && dev < 64;
-  if (cached) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) {
-      *n = c;
-      return hipSuccess;
-    }
-  }
-  int c = 0;
-  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  if (c < 1) c = 1;
-  if (cached) cache[dev].store(c, std::memory_order_relaxed);
-  *n = c;
-  return hipSuccess;
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

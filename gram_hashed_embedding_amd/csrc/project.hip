@@ -291,7 +291,7 @@ template <int MT, int NC, int R, int U, int SK>
 __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ B,
                                                                uint16_t* __restrict__ C, int M,
-                                                               int N) {
+                                                               int N, int RW) {
   constexpr int KS = K / SK;                 // super-steps
   constexpr int J = SK / 32;                 // MFMA K-steps per super-step
   constexpr int CH = SK / 8;                 // 16-byte chunks per row per super-step
@@ -346,10 +346,15 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
   }
 
   // ---- consumers
-  const int n0 = blockIdx.x * (16 * NC) + (wave - 1) * 16;
+  // Workgroup w owns wkv rows [w*RW, w*RW + RW); rows of its last 16-row
+  // tile past that range re-read its last row (same lines: no extra HBM
+  // traffic) and are not stored.
+  const int base = blockIdx.x * RW;
+  const int lim = (base + RW) < N ? (base + RW) : N;
+  const int n0 = base + (wave - 1) * 16;
   const int arow = lane & 15, g = lane >> 4;
   int nr = n0 + arow;
-  nr = nr < N ? nr : N - 1;
+  nr = nr < lim ? nr : lim - 1;
   const uint16_t* bp = B + (int64_t)nr * K + g * J * 8;   // this lane's SK/4-value span
   bf16x8 bq[U][J];
 #pragma unroll
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
 
   // 16x16 accumulator layout: lane holds column lane & 15 and rows 4*(lane >> 4) + jj.
   const int col = n0 + arow;
-  if (col < N) {
+  if (col < lim) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -399,11 +404,19 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
   }
 }
 
+// One workgroup per CU, each with an equal share of wkv rows (100 of 25,600
+// on 256 CUs): workgroups of a fixed 16*NC rows left CUs idle or doubly
+// loaded (25,600 rows are 6.25 tiles of 16 per CU), which cost 8-22%.
 template <int MT, int NC, int R, int U, int SK>
 hipError_t run_skinny(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N, uint16_t* kv,
                       hipStream_t st) {
-  const int blocks = (N + 16 * NC - 1) / (16 * NC);
-  skinny_kernel<MT, NC, R, U, SK><<<blocks, 64 * (NC + 1), 0, st>>>(mem, wkv, kv, (int)T, N);
+  int n_cu = 0;
+  hipError_t e = cu_count(&n_cu);
+  if (e != hipSuccess) return e;
+  int rw = (N + n_cu - 1) / n_cu;
+  rw = rw < 16 ? 16 : (rw > 16 * NC ? 16 * NC : rw);
+  const int blocks = (N + rw - 1) / rw;
+  skinny_kernel<MT, NC, R, U, SK><<<blocks, 64 * (NC + 1), 0, st>>>(mem, wkv, kv, (int)T, N, rw);
   return hipGetLastError();
 }
 
@@ -420,11 +433,11 @@ hipError_t run_wave_tile(const uint16_t* mem, int64_t T, const uint16_t* wkv, in
 hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
                           uint16_t* kv, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  // <MT, NC, R, U, SK> chosen by a sweep on the 25,600 x 6,144 wkv stream
-  if (T <= 16) return run_skinny<1, 4, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 32) return run_skinny<2, 4, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 64) return run_skinny<4, 8, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 128) return run_skinny<8, 4, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  // <MT, NC, R, U, SK> chosen by sweeps on the 25,600 x 6,144 wkv stream
+  if (T <= 16) return run_skinny<1, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 32) return run_skinny<2, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 64) return run_skinny<4, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 128) return run_skinny<8, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
   return run_wave_tile(mem, T, wkv, N, kv, st);
 }
 
