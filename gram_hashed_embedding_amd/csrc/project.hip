@@ -16,14 +16,15 @@
 // both operands in L2.
 //
 // Two kernels:
-//  - wave_tile_kernel (T > 128): 256 x 256 x 64 tiles, 4 waves of 128 x 128
+//  - wave_tile_kernel (T > 256): 256 x 256 x 64 tiles, 4 waves of 128 x 128
 //    each, loads staged through registers two K steps ahead and spread
 //    between the MFMAs.
-//  - skinny_kernel (T <= 128): the projection is a stream of wkv; the few mem
+//  - skinny_kernel (T <= 256): the projection is a stream of wkv; the few mem
 //    rows sit in LDS and wkv rows go straight into registers.
-// Measured on the 25,600 x 6,144 wkv: the 256 x 256 kernel takes 128-157 us
-// for T = 160..512, where 16-row skinny tiles (LDS-bound from T ~ 160) and
-// 128 x 128 tiles took 160-255 us.
+// Measured on the 25,600 x 6,144 wkv: the skinny kernel takes 78 / 95 / 104-117
+// us at T = 64 / 128 / 160-256, where the 256 x 256 kernel takes 128-147 us;
+// above T = 256 the 256 x 256 kernel wins (141-158 us at T = 384-512, where
+// 128 x 128 tiles took 233-255 us).
 
 #include "engram_internal.h"
 
@@ -438,6 +439,8 @@ hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, i
   if (T <= 32) return run_skinny<2, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
   if (T <= 64) return run_skinny<4, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
   if (T <= 128) return run_skinny<8, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 192) return run_skinny<12, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
+  if (T <= 256) return run_skinny<16, 7, 3, 8, 64>(mem, T, wkv, N, kv, st);
   return run_wave_tile(mem, T, wkv, N, kv, st);
 }
 

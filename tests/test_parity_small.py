@@ -190,10 +190,10 @@ def _mem_from_tiny(T, seed=0):
     return O.gather_decode(idx, w.rows(0))
 
 
-@pytest.mark.parametrize("T", [1, 16, 17, 33, 63, 64, 65, 128, 129, 300])
+@pytest.mark.parametrize("T", [1, 16, 17, 33, 63, 64, 65, 128, 129, 192, 193, 256, 257, 300])
 def test_project_tiny_widths(E, T):
-    """Every skinny configuration (T <= 16, 32, 64, 128) and the switch to
-    256 x 256 tiles above T = 128, each at its edges."""
+    """Every skinny configuration (T <= 16, 32, 64, 128, 192, 256) and the
+    switch to 256 x 256 tiles above T = 256, each at its edges."""
     log(f"project: tiny wkv (1,280 x 6,144), T={T}")
     cfg = synth.CONFIGS["tiny"]
     wkv = synth.wkv_bf16(cfg, 1)
@@ -266,7 +266,7 @@ def test_project_full_size_sampled_rows(E):
     assert_bf16_close(got, O.project(mem[rows], wkv), what="kv")
 
 
-@pytest.mark.parametrize("T", [64, 128, 129, 256, 257])
+@pytest.mark.parametrize("T", [64, 128, 129, 192, 256, 257])
 def test_project_full_width(E, T):
     log(f"project: full wkv 25,600 x 6,144, T={T}")
     cfg = synth.CONFIGS["decode"]
