@@ -396,3 +396,45 @@ def test_forward_decode_config(E):
     got, (wkv, wqk) = _run_forward(E, w, 0, tok, cu, hist, hidden)
     ref = O.forward(tok, cu, hist, w.tmap, p, w.rows(0), wkv, wqk, hidden, cfg.H, cfg.hc)
     _check_forward(got, ref, cfg.hc, cfg.H)
+
+
+def test_two_layers_on_a_side_stream_match_one_stream(E):
+    """Running one layer's engram_forward on a side stream beside another's
+    (both read the same history; the append waits for both) gives the same
+    hidden states and history, bit for bit, as running them in turn on one
+    stream, over several decode steps."""
+    log("forward: two layers, side stream vs one stream, 3 decode steps")
+    w = World.of("decode")
+    cfg, p = w.cfg, w.params[0]
+    codes, scales = device_table(E, p.n_rows, *w.keys[0])
+    wkv = up16(synth.wkv_bf16(cfg, 1))
+    wqk = torch.from_numpy(synth.norm_weights(cfg, 1)).to(DEV)
+    tmap = up32(w.tmap)
+    S = cfg.n_seqs
+    cu = up32(np.arange(S + 1, dtype=np.int32))
+    ptok, pcu = synth.history_prefix_tokens(cfg)
+    toks = [up32(synth.decode_tokens(cfg, s)) for s in range(3)]
+    runs = []
+    for mode in ("one", "side"):
+        hist = torch.empty(S * 3, dtype=torch.int32, device=DEV)
+        E.engram_history_reset(hist, p.pad_cid)
+        E.engram_history_append(hist, up32(ptok), up32(pcu), tmap, p.pad_cid)
+        hidden = [up16(synth.hidden_bf16(cfg, layer, S)) for layer in (1, 2)]
+        ws = [torch.empty(E.engram_forward_workspace(S, cfg.H, cfg.hc), dtype=torch.uint8, device=DEV)
+              for _ in range(2)]
+        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        for tok in toks:
+            if mode == "side":
+                side.wait_stream(main)
+            for li in (1, 0):
+                st = side if (mode == "side" and li == 1) else main
+                E.engram_forward(tok, cu, hist, tmap, p, codes, scales, wkv, wqk, hidden[li],
+                                 cfg.H, cfg.hc, ws=ws[li], stream=st)
+            if mode == "side":
+                main.wait_stream(side)
+            E.engram_history_append(hist, tok, cu, tmap, p.pad_cid, stream=main)
+        torch.cuda.synchronize()
+        runs.append((down32(hist), [down16(h) for h in hidden]))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    for a, b in zip(runs[0][1], runs[1][1]):
+        assert np.array_equal(a, b)
