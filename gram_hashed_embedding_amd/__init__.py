@@ -121,8 +121,10 @@ def _torch():
     return torch
 
 
-def _ptr(t, dtype=None, name="tensor", optional=False):
-    """Device pointer of a contiguous CUDA(HIP) tensor (or None -> NULL)."""
+def _ptr(t, dtype=None, name="tensor", optional=False, host_ok=False):
+    """Device pointer of a contiguous CUDA(HIP) tensor (or None -> NULL).
+    With host_ok, a pinned host tensor is accepted too: pinned memory is
+    mapped into the device's address space at its host address."""
     if t is None:
         if optional:
             return None
@@ -130,8 +132,9 @@ def _ptr(t, dtype=None, name="tensor", optional=False):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_cuda and not (host_ok and t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor" + (" or a pinned host tensor" if host_ok else "")
+                         + f" (got {t.device})")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
@@ -237,8 +240,8 @@ def engram_gather_decode(idx, codes, scales, n_rows: int, mem, err_flags=None, s
     _need(scales, n_rows * 8, "scales")
     _need(err_flags, 1, "err_flags")
     _check(lib.engram_gather_decode(
-        _ptr(idx, _u32(torch), "idx"), T, _ptr(codes, torch.uint8, "codes"),
-        _ptr(scales, torch.uint8, "scales"), n_rows, _ptr(mem, _u16(torch), "mem"),
+        _ptr(idx, _u32(torch), "idx"), T, _ptr(codes, torch.uint8, "codes", host_ok=True),
+        _ptr(scales, torch.uint8, "scales", host_ok=True), n_rows, _ptr(mem, _u16(torch), "mem"),
         _ptr(err_flags, _u32(torch), "err_flags", optional=True), _stream(stream)),
         "engram_gather_decode")
 
@@ -311,8 +314,8 @@ def engram_forward(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv,
     _check(lib.engram_forward(
         _ptr(tok, _u32(torch), "tok"), _ptr(cu_seqlens, _i32(torch), "cu_seqlens"), S, T,
         _ptr(hist, _u32(torch), "hist"), _ptr(token_map, _u32(torch), "token_map"),
-        token_map.numel(), ctypes.byref(p), _ptr(codes, torch.uint8, "codes"),
-        _ptr(scales, torch.uint8, "scales"), _ptr(wkv, _u16(torch), "wkv"),
+        token_map.numel(), ctypes.byref(p), _ptr(codes, torch.uint8, "codes", host_ok=True),
+        _ptr(scales, torch.uint8, "scales", host_ok=True), _ptr(wkv, _u16(torch), "wkv"),
         _ptr(wqk, torch.float32, "wqk"), _ptr(hidden, _u16(torch), "hidden"), H, hc, eps,
         dot_scale, _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _ptr(gate_out, torch.float32, "gate_out", optional=True),
@@ -327,6 +330,6 @@ def engram_gen_table(codes, scales, row_begin: int, n_rows: int, key_data: int, 
     torch = _torch()
     if codes.numel() < n_rows * 256 or scales.numel() < n_rows * 8:
         raise ValueError("codes/scales too small for n_rows")
-    _check(lib.engram_gen_table(_ptr(codes, torch.uint8, "codes"), _ptr(scales, torch.uint8, "scales"),
+    _check(lib.engram_gen_table(_ptr(codes, torch.uint8, "codes", host_ok=True), _ptr(scales, torch.uint8, "scales", host_ok=True),
                                 row_begin, n_rows, key_data, key_scale, _stream(stream)),
            "engram_gen_table")

@@ -35,6 +35,23 @@ int from_hip(hipError_t e, const char* what) {
   return fail(ENGRAM_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A table lives either in device memory or in pinned host memory that the
+// runtime maps into the device's address space at its host address
+// (hipHostMalloc); its rows then cross the host link on every read.
+int check_table_memory(const void* p, const char* what) {
+  hipPointerAttribute_t a;
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();   // not sticky: the next launch check must not see it
+    return fail(ENGRAM_EINVAL, "%s: not device memory or pinned host memory (%s)", what,
+                hipGetErrorString(e));
+  }
+  if (a.type == hipMemoryTypeDevice) return ENGRAM_OK;
+  if (a.type == hipMemoryTypeHost && a.devicePointer == p) return ENGRAM_OK;
+  return fail(ENGRAM_EINVAL, "%s: memory type %d is not device memory or pinned host memory mapped at "
+              "its host address", what, (int)a.type);
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Deterministic Miller-Rabin for 32-bit n (bases 2, 7, 61 suffice below 4,759,123,141).
@@ -275,6 +292,10 @@ int engram_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin, uint64
     if (!codes || !scales) return fail(ENGRAM_EINVAL, "NULL pointer");
     if (!aligned(codes, 16) || !aligned(scales, 8))
       return fail(ENGRAM_EINVAL, "codes 16-byte and scales 8-byte alignment required");
+    const int rc_c = check_table_memory(codes, "codes");
+    if (rc_c != ENGRAM_OK) return rc_c;
+    const int rc_s = check_table_memory(scales, "scales");
+    if (rc_s != ENGRAM_OK) return rc_s;
   }
   return from_hip(engram::launch_gen_table(codes, scales, row_begin, n_rows, key_data, key_scale, stream),
                   "engram_gen_table");

@@ -148,7 +148,12 @@ int engram_hash(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64
  * sign(code)|0x7FC0 ([zLLM] 第二步: read only the selected rows and their
  * scales; [Storage]: FP8 E4M3 with UE8M0 group-32 scales decoded to BF16).
  * ENGRAM_DEAD_IDX rows give zeros. codes: uint8[n_rows][256] (16-byte
- * aligned), scales: uint8[n_rows][8] (8-byte aligned), mem 16-byte aligned. */
+ * aligned), scales: uint8[n_rows][8] (8-byte aligned), mem 16-byte aligned.
+ * The table (codes and scales, here and in engram_forward) may be device
+ * memory or pinned host memory that is mapped into the device's address
+ * space at its host address (hipHostMalloc); the rows then cross the host
+ * link, as with the pages' host-resident tables ([vLLM] CPU offload). Other
+ * host memory must not be passed: the kernels read it directly. */
 int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                          const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
                          uint32_t* err_flags, hipStream_t stream);
@@ -209,7 +214,9 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
  * where F lists the 254 non-NaN E4M3 codes in ascending order and
  * splitmix64(x) is the first output of a SplitMix64 generator (Steele, Lea
  * and Flood, 2014) whose state is x. `codes` and `scales` point at row
- * row_begin (16- and 8-byte aligned). */
+ * row_begin (16- and 8-byte aligned), in device memory or in pinned host
+ * memory mapped at its host address; anything else is rejected with
+ * ENGRAM_EINVAL before the launch. */
 int engram_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin, uint64_t n_rows,
                      uint64_t key_data, uint64_t key_scale, hipStream_t stream);
 

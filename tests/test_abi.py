@@ -135,3 +135,14 @@ def test_workspace_size_formula(E):
     r = lambda x: (x + 255) // 256 * 256
     assert E.engram_forward_workspace(T, H, hc) == r(T * 96) + r(T * 12288) + r(T * 25600 * 2)
     assert E.engram_forward_workspace(0, H, hc) == 0
+
+
+def test_table_pointers_accept_pinned_host_memory_only(E):
+    """Tables may be pinned host memory (mapped into the device's address
+    space); plain host memory is refused by the binding before any call."""
+    import torch
+    plain = torch.zeros(256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="pinned host tensor"):
+        E._ptr(plain, torch.uint8, "codes", host_ok=True)
+    with pytest.raises(ValueError, match="device tensor"):
+        E._ptr(plain, torch.uint8, "mem")

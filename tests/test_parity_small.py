@@ -438,3 +438,49 @@ def test_two_layers_on_a_side_stream_match_one_stream(E):
     assert np.array_equal(runs[0][0], runs[1][0])
     for a, b in zip(runs[0][1], runs[1][1]):
         assert np.array_equal(a, b)
+
+
+def test_host_resident_table_matches_device_table(E):
+    """The decode config's 16M-row table in pinned host memory (mapped into
+    the device's address space; rows read across the host link) gives the
+    same gathered rows and the same decode step as the table in HBM."""
+    log("gather + forward: decode config with its table in pinned host memory")
+    w = World.of("decode")
+    cfg, p = w.cfg, w.params[0]
+    codes_h = torch.empty(p.n_rows * 256, dtype=torch.uint8, pin_memory=True)
+    scales_h = torch.empty(p.n_rows * 8, dtype=torch.uint8, pin_memory=True)
+    try:
+        E.engram_gen_table(codes_h, scales_h, 0, p.n_rows, *w.keys[0])
+    except E.EngramError as e:
+        pytest.skip(f"pinned host memory is not mapped for the device here: {e}")
+    codes_d, scales_d = device_table(E, p.n_rows, *w.keys[0])
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(7).integers(0, p.n_rows, 64)
+    for r in rows:
+        assert torch.equal(codes_h[r * 256:(r + 1) * 256], codes_d[r * 256:(r + 1) * 256].cpu())
+        assert torch.equal(scales_h[r * 8:(r + 1) * 8], scales_d[r * 8:(r + 1) * 8].cpu())
+    S = cfg.n_seqs
+    ptok, pcu = synth.history_prefix_tokens(cfg)
+    tmap = up32(w.tmap)
+    cu = up32(np.arange(S + 1, dtype=np.int32))
+    tok = up32(synth.decode_tokens(cfg, 0))
+    hist = torch.empty(S * 3, dtype=torch.int32, device=DEV)
+    E.engram_history_reset(hist, p.pad_cid)
+    E.engram_history_append(hist, up32(ptok), up32(pcu), tmap, p.pad_cid)
+    idx = torch.empty(S * 24, dtype=torch.int32, device=DEV)
+    E.engram_hash(tok, cu, hist, tmap, p, idx)
+    mem_h = torch.empty(S * 6144, dtype=torch.int16, device=DEV)
+    mem_d = torch.empty_like(mem_h)
+    E.engram_gather_decode(idx, codes_h, scales_h, p.n_rows, mem_h)
+    E.engram_gather_decode(idx, codes_d, scales_d, p.n_rows, mem_d)
+    torch.cuda.synchronize()
+    assert torch.equal(mem_h, mem_d)
+    wkv = up16(synth.wkv_bf16(cfg, 1))
+    wqk = torch.from_numpy(synth.norm_weights(cfg, 1)).to(DEV)
+    outs = []
+    for codes, scales in ((codes_h, scales_h), (codes_d, scales_d)):
+        hidden = up16(synth.hidden_bf16(cfg, 1, S))
+        E.engram_forward(tok, cu, hist, tmap, p, codes, scales, wkv, wqk, hidden, cfg.H, cfg.hc)
+        torch.cuda.synchronize()
+        outs.append(down16(hidden))
+    assert np.array_equal(outs[0], outs[1])
