@@ -192,6 +192,59 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
   }
 }
 
+// Small-T variant for H = 8 * THREADS: one workgroup per (token, branch),
+// so a decode batch of 64 tokens fills 256 workgroups instead of 64. Each
+// branch's gate needs only that branch's hidden and key (and every branch
+// the shared value, read once per branch). Thread i owns chunk i, and the
+// sums are formed and reduced in the same order as in gate_stream_kernel,
+// so the two kernels give identical bits.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void gate_branch_kernel(
+    uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
+    const uint32_t* __restrict__ tok, int hc, float eps, float dot_scale,
+    float* __restrict__ gate_out) {
+  constexpr int WAVES = THREADS / 64;
+  constexpr int H = THREADS * 8;
+  const int64_t t = blockIdx.x / hc;
+  const int b = blockIdx.x - (int)t * hc;
+  const int tid = threadIdx.x;
+  if (tok != nullptr && tok[t] == ENGRAM_DEAD_TOKEN) {
+    if (gate_out != nullptr && tid == 0) gate_out[t * hc + b] = 0.0f;
+    return;
+  }
+  uint16_t* h_t = hidden + (t * hc + b) * (int64_t)H + tid * 8;
+  const uint16_t* kv_t = kv + t * (int64_t)(hc + 1) * H + tid * 8;
+  const uint4 hq = nt_load(h_t);
+  const uint4 kq = nt_load(kv_t + b * H);
+  const uint4 vq = nt_load(kv_t + hc * H);
+  const float4 w0 = *reinterpret_cast<const float4*>(wqk + b * H + tid * 8);
+  const float4 w1 = *reinterpret_cast<const float4*>(wqk + b * H + tid * 8 + 4);
+  const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float h[8], k[8];
+  unpack8(hq, h);
+  unpack8(kq, k);
+  float s[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s[0] = fmaf(h[i], h[i], s[0]);
+    s[1] = fmaf(k[i], k[i], s[1]);
+    s[2] = fmaf(h[i] * k[i], w[i], s[2]);
+  }
+  __shared__ float red[3 * WAVES];
+  __shared__ float g_sh[1];
+  reduce_gates<1, WAVES>(s, red, g_sh, H, eps, dot_scale, nullptr, 0);
+  const float g = g_sh[0];
+  if (gate_out != nullptr && tid == 0) gate_out[t * hc + b] = g;
+  float v[8];
+  unpack8(vq, v);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_bf16_rne(fmaf(g, v[2 * i], h[2 * i])) |
+           (f32_to_bf16_rne(fmaf(g, v[2 * i + 1], h[2 * i + 1])) << 16);
+  nt_store(h_t, o[0], o[1], o[2], o[3]);
+}
+
 // Generic variant (any H % 64 == 0, hc <= 8): 256 threads, strided chunks,
 // hidden and value re-read (from L2) for the residual.
 constexpr int kGenThreads = 256;
@@ -280,19 +333,27 @@ hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
                        const uint32_t* tok, int64_t T, int32_t H, int32_t hc, float eps,
                        float dot_scale, float* gate_out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  if (hc == 4 && H == 5120) {
-    // one resident workgroup per CU (the kernel keeps two tokens' loads in
-    // registers, so a second workgroup would not fit beside it)
+  if (H == 5120) {
     int n_cu = 0;
     hipError_t e = cu_count(&n_cu);
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)(T < n_cu ? T : n_cu);
-    gate_stream_kernel<4, 640><<<grid, 640, 0, st>>>(hidden, kv, wqk, tok, T, eps, dot_scale,
-                                                     gate_out);
-  } else {
-    gate_generic_kernel<<<(unsigned)T, kGenThreads, 0, st>>>(hidden, kv, wqk, tok, H, hc, eps,
-                                                             dot_scale, gate_out);
+    if ((hc != 4 || T * hc <= 4 * (int64_t)n_cu) && T * hc <= (int64_t)INT32_MAX) {
+      // decode-sized batches (and other branch counts): a workgroup per (token, branch)
+      gate_branch_kernel<640><<<(unsigned)(T * hc), 640, 0, st>>>(hidden, kv, wqk, tok, hc, eps,
+                                                                  dot_scale, gate_out);
+      return hipGetLastError();
+    }
+    if (hc == 4) {
+      // one resident workgroup per CU (the kernel keeps two tokens' loads in
+      // registers, so a second workgroup would not fit beside it)
+      const unsigned grid = (unsigned)(T < n_cu ? T : n_cu);
+      gate_stream_kernel<4, 640><<<grid, 640, 0, st>>>(hidden, kv, wqk, tok, T, eps, dot_scale,
+                                                       gate_out);
+      return hipGetLastError();
+    }
   }
+  gate_generic_kernel<<<(unsigned)T, kGenThreads, 0, st>>>(hidden, kv, wqk, tok, H, hc, eps,
+                                                           dot_scale, gate_out);
   return hipGetLastError();
 }
 
