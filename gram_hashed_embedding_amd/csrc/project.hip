@@ -37,6 +37,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int K = ENGRAM_MEM;
 constexpr int BK = 64;
 constexpr int kXcds = 8;
+// Fourth word of a raw buffer resource on gfx9-family GPUs: a 32-bit data
+// format, so the hardware accepts the buffer loads (raw loads with stride 0
+// ignore the format otherwise).
+constexpr int kRawBufferWord3 = 0x00020000;
 
 // ---------------------------------------------------------------- wave-tile kernel
 // Tile 256 x 256 x 64, 4 waves (one per SIMD), each owning a 128 x 128
@@ -123,9 +127,9 @@ __global__ __launch_bounds__(256) void wave_tile_kernel(const uint16_t* __restri
   const int rowsA = (M - m0) < BM ? (M - m0) : BM;
   const int rowsB = (N - n0) < BN ? (N - n0) : BN;
   const auto rsA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A) + (int64_t)m0 * K, 0,
-                                                    rowsA * K * 2, 0x00020000);
+                                                    rowsA * K * 2, kRawBufferWord3);
   const auto rsB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B) + (int64_t)n0 * K, 0,
-                                                    rowsB * K * 2, 0x00020000);
+                                                    rowsB * K * 2, kRawBufferWord3);
   const int gr = tid >> 3, gc = tid & 7;
   int voffA[8], voffB[8];
 #pragma unroll
