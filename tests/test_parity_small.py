@@ -251,15 +251,19 @@ def test_project_large_t_ragged_n(E):
 
 def test_project_full_size_sampled_rows(E):
     """4,096 tokens x full wkv (the full-size prefill shape): rows sampled at
-    tile edges and at random are compared with the oracle."""
+    tile edges and at random are compared with the oracle. The 1,600 tiles
+    are six full groups of 256 in the XCD-interleaved order plus a partial
+    group in plain order; kv starts as NaN, and no NaN may survive, so every
+    tile was written."""
     log("project: 4,096 x 25,600 x 6,144, sampled rows")
     cfg = synth.CONFIGS["full"]
     T = 4096
     wkv = synth.wkv_bf16(cfg, 1)
     rng = np.random.default_rng(11)
     mem = synth.bf16_bits_from_f32(rng.standard_normal((T, 6144)).astype(np.float32) * 0.1)
-    kv = torch.empty(T * 25600, dtype=torch.int16, device=DEV)
+    kv = torch.full((T * 25600,), 0x7FC1, dtype=torch.int16, device=DEV)
     E.engram_project(up16(mem), up16(wkv), cfg.H, cfg.hc, kv)
+    assert not torch.isnan(kv.view(torch.bfloat16)).any().item(), "tile left unwritten"
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 257, 2047, 2048, 4094, 4095],
                                      rng.integers(0, T, 53)]))
     got = down16(kv).reshape(T, -1)[rows]
