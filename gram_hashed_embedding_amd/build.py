@@ -20,7 +20,8 @@ OBJ = os.path.join(ROOT, "_build", "engram")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["engram_api.cpp", "hash.hip", "gather.hip", "project.hip", "gate.hip", "gentable.hip"]
+SOURCES = ["engram_api.cpp", "hash.hip", "gather.hip", "hash_gather.hip", "project.hip", "gate.hip",
+           "gentable.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           # keep the compiler from forming packed FP32 instructions

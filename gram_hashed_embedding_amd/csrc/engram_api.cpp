@@ -121,6 +121,36 @@ int check_dims(int32_t H, int32_t hc) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Host checks of engram_hash's arguments (also applied by engram_forward).
+int check_hash_args(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                    const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                    const engram_hash_params* params, const uint32_t* idx) {
+  int rc = check_struct(params);
+  if (rc != ENGRAM_OK) return rc;
+  rc = check_tokens(tok, cu_seqlens, S, T);
+  if (rc != ENGRAM_OK) return rc;
+  if (T > 0) {
+    if (hist == nullptr || idx == nullptr || token_map == nullptr || map_len == 0)
+      return fail(ENGRAM_EINVAL, "hist, idx or token_map missing");
+    if (!aligned(hist, 4) || !aligned(idx, 4) || !aligned(token_map, 4))
+      return fail(ENGRAM_EINVAL, "hist/idx/token_map not 4-byte aligned");
+  }
+  return ENGRAM_OK;
+}
+
+// Host checks of engram_gather_decode's arguments (also applied by engram_forward).
+int check_gather_args(const uint32_t* idx, int64_t T, const uint8_t* codes, const uint8_t* scales,
+                      uint64_t n_rows, const uint16_t* mem) {
+  if (T < 0 || T > (int64_t)INT32_MAX) return fail(ENGRAM_EINVAL, "T out of range");
+  if (T > 0) {
+    if (!idx || !codes || !scales || !mem) return fail(ENGRAM_EINVAL, "NULL pointer");
+    if (n_rows == 0 || n_rows >= 0xFFFFFFFFull) return fail(ENGRAM_EINVAL, "n_rows out of range");
+    if (!aligned(idx, 4) || !aligned(codes, 16) || !aligned(scales, 8) || !aligned(mem, 16))
+      return fail(ENGRAM_EINVAL, "idx 4-, codes 16-, scales 8-, mem 16-byte alignment required");
+  }
+  return ENGRAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,16 +211,8 @@ int engram_hash(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64
                 const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
                 const engram_hash_params* params, uint32_t* idx, uint32_t* err_flags,
                 hipStream_t stream) {
-  int rc = check_struct(params);
+  const int rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx);
   if (rc != ENGRAM_OK) return rc;
-  rc = check_tokens(tok, cu_seqlens, S, T);
-  if (rc != ENGRAM_OK) return rc;
-  if (T > 0) {
-    if (hist == nullptr || idx == nullptr || token_map == nullptr || map_len == 0)
-      return fail(ENGRAM_EINVAL, "hist, idx or token_map missing");
-    if (!aligned(hist, 4) || !aligned(idx, 4) || !aligned(token_map, 4))
-      return fail(ENGRAM_EINVAL, "hist/idx/token_map not 4-byte aligned");
-  }
   return from_hip(engram::launch_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, *params,
                                       idx, err_flags, stream),
                   "engram_hash");
@@ -199,13 +221,8 @@ int engram_hash(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64
 int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                          const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
                          uint32_t* err_flags, hipStream_t stream) {
-  if (T < 0 || T > (int64_t)INT32_MAX) return fail(ENGRAM_EINVAL, "T out of range");
-  if (T > 0) {
-    if (!idx || !codes || !scales || !mem) return fail(ENGRAM_EINVAL, "NULL pointer");
-    if (n_rows == 0 || n_rows >= 0xFFFFFFFFull) return fail(ENGRAM_EINVAL, "n_rows out of range");
-    if (!aligned(idx, 4) || !aligned(codes, 16) || !aligned(scales, 8) || !aligned(mem, 16))
-      return fail(ENGRAM_EINVAL, "idx 4-, codes 16-, scales 8-, mem 16-byte alignment required");
-  }
+  const int rc = check_gather_args(idx, T, codes, scales, n_rows, mem);
+  if (rc != ENGRAM_OK) return rc;
   return from_hip(engram::launch_gather_decode(idx, T, codes, scales, n_rows, mem, err_flags, stream),
                   "engram_gather_decode");
 }
@@ -272,11 +289,27 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
     return from_hip(hipEventRecord(stage_events[i], stream), "engram_forward: hipEventRecord");
   };
   if ((rc = mark(0)) != ENGRAM_OK) return rc;
-  rc = engram_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx, err_flags, stream);
-  if (rc != ENGRAM_OK) return rc;
-  if ((rc = mark(1)) != ENGRAM_OK) return rc;
-  rc = engram_gather_decode(idx, T, codes, scales, params->n_rows, mem, err_flags, stream);
-  if (rc != ENGRAM_OK) return rc;
+  if (T <= engram::kHashGatherMaxTokens && S <= engram::kHashGatherMaxSeqs) {
+    // Small batch: one kernel hashes, gathers and decodes; stage events 1
+    // and 2 both mark its end.
+    rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx);
+    if (rc != ENGRAM_OK) return rc;
+    rc = check_gather_args(idx, T, codes, scales, params->n_rows, mem);
+    if (rc != ENGRAM_OK) return rc;
+    if (T > 0) {
+      rc = from_hip(engram::launch_hash_gather(tok, cu_seqlens, S, T, hist, token_map, map_len,
+                                               *params, codes, scales, idx, mem, err_flags, stream),
+                    "engram_forward: hash + gather");
+      if (rc != ENGRAM_OK) return rc;
+    }
+    if ((rc = mark(1)) != ENGRAM_OK) return rc;
+  } else {
+    rc = engram_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx, err_flags, stream);
+    if (rc != ENGRAM_OK) return rc;
+    if ((rc = mark(1)) != ENGRAM_OK) return rc;
+    rc = engram_gather_decode(idx, T, codes, scales, params->n_rows, mem, err_flags, stream);
+    if (rc != ENGRAM_OK) return rc;
+  }
   if ((rc = mark(2)) != ENGRAM_OK) return rc;
   rc = engram_project(mem, T, wkv, H, hc, kv, stream);
   if (rc != ENGRAM_OK) return rc;

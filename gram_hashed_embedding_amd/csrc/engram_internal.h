@@ -25,6 +25,17 @@ hipError_t launch_hash(const uint32_t* tok, const int32_t* cu, int32_t S, int64_
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                                 const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
                                 uint32_t* err, hipStream_t st);
+// Hash, gather and decode as one kernel (hash_gather.hip): for batches of at
+// most kHashGatherMaxTokens tokens in at most kHashGatherMaxSeqs sequences,
+// where both steps are latency-bound chains of loads. Writes the same idx and
+// mem as launch_hash followed by launch_gather_decode.
+constexpr int64_t kHashGatherMaxTokens = 1024;
+constexpr int32_t kHashGatherMaxSeqs = 1024;
+hipError_t launch_hash_gather(const uint32_t* tok, const int32_t* cu, int32_t S, int64_t T,
+                              const uint32_t* hist, const uint32_t* map, uint32_t map_len,
+                              const engram_hash_params& p, const uint8_t* codes,
+                              const uint8_t* scales, uint32_t* idx, uint16_t* mem, uint32_t* err,
+                              hipStream_t st);
 hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
                           uint16_t* kv, hipStream_t st);
 hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,

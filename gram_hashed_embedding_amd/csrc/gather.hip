@@ -15,7 +15,7 @@
 // Each lane keeps kRowsInFlight rows' loads outstanding before decoding to
 // cover the latency of random HBM reads.
 
-#include "engram_internal.h"
+#include "decode_device.h"
 
 namespace engram {
 namespace {
@@ -23,31 +23,6 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kGroups = kBlock / 16;     // rows per pass of one workgroup
 constexpr int kRowsInFlight = 4;         // passes per workgroup (rows per lane)
-
-// Exact E4M3 x 2^(s-127) -> BF16, two codes at a time, on the gfx950
-// scaled-convert unit: v_cvt_scalef32_pk_bf16_fp8 multiplies each OCP E4M3
-// code by the power of two held in the exponent field of its float scale
-// operand (for a scale byte s that is the float with bits s << 23, so s = 0
-// and s = 255 need no special case) and rounds to BF16. Its results are exact
-// for every finite code and scale, BF16 subnormals included; every NaN it
-// produces is 0xFFC0. The method keeps each value's sign from its code, so
-// the sign bits are re-applied from the codes: a no-op for all non-NaN
-// results, and it turns NaNs into sign(code)|0x7FC0.
-template <bool HI>
-__device__ __forceinline__ uint32_t decode2(uint32_t w, float scale) {
-  const auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
-  const uint32_t bits = __builtin_bit_cast(uint32_t, r);
-  const uint32_t b = HI ? (w >> 16) : w;                      // the two codes in bytes 0, 1
-  const uint32_t signs = ((b << 8) & 0x8000u) | ((b << 16) & 0x80000000u);
-  return (bits & 0x7FFF7FFFu) | signs;
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void nt_store16(uint16_t* p, uint32_t a, uint32_t b, uint32_t c,
-                                           uint32_t d) {
-  const u32x4 v = {a, b, c, d};
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-}
 
 __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
     const uint32_t* __restrict__ idx, int64_t total_rows, const uint8_t* __restrict__ codes,
@@ -90,17 +65,7 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
   for (int u = 0; u < kRowsInFlight; ++u) {
     const int64_t r = base + u * kGroups + grp;
     if (r >= total_rows) continue;
-    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-    if (live[u]) {
-      const float s0 = __uint_as_float(sa[u] << 23), s1 = __uint_as_float(sb[u] << 23);
-      a = make_uint4(decode2<false>(ca[u].x, s0), decode2<true>(ca[u].x, s0),
-                     decode2<false>(ca[u].y, s0), decode2<true>(ca[u].y, s0));
-      b = make_uint4(decode2<false>(cb[u].x, s1), decode2<true>(cb[u].x, s1),
-                     decode2<false>(cb[u].y, s1), decode2<true>(cb[u].y, s1));
-    }
-    uint16_t* out = mem + r * ENGRAM_ROW;
-    nt_store16(out + l * 8, a.x, a.y, a.z, a.w);
-    nt_store16(out + 128 + l * 8, b.x, b.y, b.z, b.w);
+    decode_store_row(mem + r * ENGRAM_ROW, l, live[u], ca[u], cb[u], sa[u], sb[u]);
   }
 }
 

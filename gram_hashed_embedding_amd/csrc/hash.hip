@@ -1,51 +1,19 @@
 // Hashing and per-sequence history for the Engram retrieval step.
 //
-// [zLLM] 第一步: token id -> compressed id -> current token and the three most
-// recent positions -> 24 hashes over 2/3/4-grams -> 24 row numbers, with
-// per-layer multipliers, prime buckets and offsets as static tables.
-// [vLLM] How it works (multi-head hashing): each (order, head) pair applies a
-// multiply-XOR hash to the compressed suffix n-gram and indexes its own
-// prime-sized bucket range.
+// [zLLM] 第一步: each token's 24 row numbers come from its compressed
+// suffix n-grams (the hash itself is in hash_device.h).
 // [zLLM] 第四步: each token enters the history once; DEAD image spans break
 // text n-grams; fork copies a session's history, reset clears it.
 //
 // Integer work only. One lane per (token, bucket): the 24 lanes of a token
 // write its 96-byte index row contiguously.
 
-#include "engram_internal.h"
+#include "hash_device.h"
 
 namespace engram {
 namespace {
 
 constexpr int kBlock = 256;
-
-// Sequence owning global token position t: the s with cu[s] <= t < cu[s+1].
-// cu values are clamped to [0, T] so a malformed list cannot send a read out
-// of bounds; inconsistencies are flagged.
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int32_t S, int64_t T,
-                                        int64_t t, uint32_t* err) {
-  int lo = 0, hi = S;  // invariant: answer in [lo, hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    int64_t c = cu[mid];
-    c = c < 0 ? 0 : (c > T ? T : c);
-    if (c <= t) lo = mid; else hi = mid;
-  }
-  if (cu[0] != 0 || cu[S] != T) set_err(err, ENGRAM_ERR_SEQLENS);
-  return lo;
-}
-
-__device__ __forceinline__ uint32_t compress(const uint32_t* __restrict__ map, uint32_t map_len,
-                                             uint32_t vocab_c, uint32_t pad_cid, uint32_t tok,
-                                             uint32_t* err) {
-  if (tok >= map_len) {
-    set_err(err, ENGRAM_ERR_TOKEN_RANGE);
-    return pad_cid;
-  }
-  const uint32_t c = map[tok];
-  if (c >= vocab_c) set_err(err, ENGRAM_ERR_MAP_RANGE);
-  return c;
-}
 
 __global__ __launch_bounds__(kBlock) void hash_kernel(
     const uint32_t* __restrict__ tok, const int32_t* __restrict__ cu, int32_t S, int64_t T,
@@ -55,44 +23,9 @@ __global__ __launch_bounds__(kBlock) void hash_kernel(
   if (g >= T * ENGRAM_BUCKETS) return;
   const int64_t t = g / ENGRAM_BUCKETS;
   const int j = (int)(g - t * ENGRAM_BUCKETS);
-  const int n = 2 + j / ENGRAM_HEADS_PER_ORDER;
-
   const uint32_t tk = tok[t];
-  if (tk == ENGRAM_DEAD_TOKEN) {
-    idx[g] = ENGRAM_DEAD_IDX;
-    return;
-  }
-  const int s = find_seq(cu, S, T, t, err);
-  int64_t start = cu[s];
-  start = start < 0 ? 0 : (start > t ? t : start);
-
-  // Window slots w_0..w_{n-1}: walk back from t. Inside the segment a DEAD
-  // ends the walk (everything behind it is PAD); before the segment the
-  // history supplies slots (it already holds PAD where a DEAD was).
-  uint64_t w[4];
-  w[0] = compress(map, map_len, p.vocab_c, p.pad_cid, tk, err);
-  bool behind_dead = false;
-  for (int k = 1; k < n; ++k) {
-    const int64_t pos = t - k;
-    uint32_t c;
-    if (behind_dead) {
-      c = p.pad_cid;
-    } else if (pos >= start) {
-      const uint32_t tp = tok[pos];
-      if (tp == ENGRAM_DEAD_TOKEN) {
-        behind_dead = true;
-        c = p.pad_cid;
-      } else {
-        c = compress(map, map_len, p.vocab_c, p.pad_cid, tp, err);
-      }
-    } else {
-      c = hist[(int64_t)s * ENGRAM_HIST + (k - 1 - (t - start))];
-    }
-    w[k] = c;
-  }
-  uint64_t x = 0;
-  for (int k = 0; k < n; ++k) x ^= w[k] * p.mult[j][k];   // products wrap mod 2^64
-  idx[g] = (uint32_t)(p.offset[j] + x % (uint64_t)p.prime[j]);
+  idx[g] = tk == ENGRAM_DEAD_TOKEN ? ENGRAM_DEAD_IDX
+                                   : bucket_row(tok, cu, S, T, hist, map, map_len, p, t, j, tk, err);
 }
 
 // One lane per sequence: the new history is the last three compressed ids of

@@ -195,9 +195,14 @@ size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
  * 256-byte aligned). Arguments mean what they mean in the stage calls.
  * Per step: call once per layer with that layer's params/table/wkv/wqk and
  * hidden, all reading the same `hist`, then engram_history_append once.
+ * For T <= 1024 tokens in S <= 1024 sequences (decode steps) hashing,
+ * gathering and decoding run as one kernel, since both steps are chains of
+ * dependent loads at that size; idx, mem and err_flags are bit-identical to
+ * the two separate calls.
  * stage_events: NULL, or ENGRAM_STAGE_EVENTS hipEvent_t created by the caller,
  * recorded before hashing, after hashing, after gather+decode, after the
- * projection and after the gate. */
+ * projection and after the gate (with the single hash + gather kernel, the
+ * second and third are both recorded after it). */
 int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
                    const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
                    const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,

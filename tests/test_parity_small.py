@@ -12,7 +12,7 @@ import engram_synth as synth
 from oracle import engram_oracle as O
 from tests.conftest import gpu_available
 from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, down32, log,
-                               up8, up16, up32, upf)
+                               up8, up16, up32, upf, workspace_views)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
@@ -400,6 +400,55 @@ def test_forward_decode_config(E):
     got, (wkv, wqk) = _run_forward(E, w, 0, tok, cu, hist, hidden)
     ref = O.forward(tok, cu, hist, w.tmap, p, w.rows(0), wkv, wqk, hidden, cfg.H, cfg.hc)
     _check_forward(got, ref, cfg.hc, cfg.H)
+
+
+def _random_cut_batch(rng, S, T, map_len, vocab_c, n_bad=0):
+    """S ragged sequences (some empty) holding T tokens, DEAD spans of 1-3
+    positions, a random non-PAD history, and n_bad token ids >= map_len."""
+    cuts = np.sort(rng.integers(0, T + 1, S - 1))
+    cu = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    tok = rng.integers(0, map_len, T).astype(np.uint32)
+    for a in rng.choice(T, size=T // 12, replace=False):
+        tok[a:a + int(rng.integers(1, 4))] = O.DEAD_TOKEN
+    if n_bad:
+        tok[rng.choice(T, size=n_bad, replace=False)] = map_len + 7
+    hist = rng.integers(0, vocab_c, (S, 3)).astype(np.uint32)
+    return tok, cu, hist
+
+
+@pytest.mark.parametrize("S,T,n_bad", [(1, 1, 0), (37, 300, 0), (64, 64, 0), (600, 1024, 0),
+                                       (37, 300, 5), (40, 1025, 0), (1025, 1030, 0)])
+def test_forward_small_batch_hash_gather_matches_stage_calls(E, S, T, n_bad):
+    """engram_forward hashes, gathers and decodes batches of up to 1,024 tokens
+    in up to 1,024 sequences with one kernel; its workspace idx and mem, and
+    its error flags, equal engram_hash followed by engram_gather_decode bit
+    for bit (ragged and empty sequences, DEAD spans, a random history, token
+    ids past the map), on both sides of both limits; idx also equals the oracle."""
+    log(f"forward: hash+gather vs stage calls, S={S} T={T} bad tokens={n_bad}")
+    w = World.of("tiny")
+    cfg, p = w.cfg, w.params[0]
+    rng = np.random.default_rng(1000 * S + T + n_bad)
+    tok, cu, hist = _random_cut_batch(rng, S, T, cfg.map_len, cfg.vocab_c, n_bad)
+    codes, scales = device_table(E, p.n_rows, *w.keys[0])
+    wkv = up16(synth.wkv_bf16(cfg, 1))
+    wqk = upf(synth.norm_weights(cfg, 1))
+    hidden = up16(synth.hidden_bf16(cfg, 1, T))
+    tok_d, cu_d, hist_d, tmap_d = up32(tok), up32(cu), up32(hist), up32(w.tmap)
+    err_f = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = E.engram_forward(tok_d, cu_d, hist_d, tmap_d, p, codes, scales, wkv, wqk, hidden,
+                          cfg.H, cfg.hc, err_flags=err_f)
+    idx_f, mem_f, _ = workspace_views(ws, T, cfg.H, cfg.hc)
+    err_s = torch.zeros(1, dtype=torch.int32, device=DEV)
+    idx_s = torch.empty(T * 24, dtype=torch.int32, device=DEV)
+    mem_s = torch.empty(T * 6144, dtype=torch.int16, device=DEV)
+    E.engram_hash(tok_d, cu_d, hist_d, tmap_d, p, idx_s, err_flags=err_s)
+    E.engram_gather_decode(idx_s, codes, scales, p.n_rows, mem_s, err_flags=err_s)
+    torch.cuda.synchronize()
+    assert int(err_f.item()) == int(err_s.item()) == (1 if n_bad else 0)
+    assert torch.equal(idx_f, idx_s)
+    assert torch.equal(mem_f, mem_s)
+    if not n_bad:
+        assert np.array_equal(down32(idx_f).reshape(T, 24), _ref_hash(tok, cu, hist, w.tmap, p))
 
 
 def test_two_layers_on_a_side_stream_match_one_stream(E):
