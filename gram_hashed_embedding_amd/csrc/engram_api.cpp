@@ -151,6 +151,36 @@ int check_gather_args(const uint32_t* idx, int64_t T, const uint8_t* codes, cons
   return ENGRAM_OK;
 }
 
+// Host checks of engram_project's arguments (also applied by engram_forward).
+int check_project_args(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t H, int32_t hc,
+                       const uint16_t* kv) {
+  int rc = check_dims(H, hc);
+  if (rc != ENGRAM_OK) return rc;
+  if (T < 0 || T > (int64_t)INT32_MAX) return fail(ENGRAM_EINVAL, "T out of range");
+  if (T > 0) {
+    if (!mem || !wkv || !kv) return fail(ENGRAM_EINVAL, "NULL pointer");
+    if (!aligned(mem, 16) || !aligned(wkv, 16) || !aligned(kv, 16))
+      return fail(ENGRAM_EINVAL, "mem, wkv and kv must be 16-byte aligned");
+  }
+  return ENGRAM_OK;
+}
+
+// Host checks of engram_gate's arguments (also applied by engram_forward).
+int check_gate_args(const uint16_t* hidden, const uint16_t* kv, const float* wqk, const uint32_t* tok,
+                    int64_t T, int32_t H, int32_t hc, float eps, const float* gate_out) {
+  int rc = check_dims(H, hc);
+  if (rc != ENGRAM_OK) return rc;
+  if (T < 0 || T > (int64_t)INT32_MAX) return fail(ENGRAM_EINVAL, "T out of range");
+  if (!(eps >= 0.0f)) return fail(ENGRAM_EINVAL, "eps must be >= 0");
+  if (T > 0) {
+    if (!hidden || !kv || !wqk) return fail(ENGRAM_EINVAL, "NULL pointer");
+    if (!aligned(hidden, 16) || !aligned(kv, 16) || !aligned(wqk, 16))
+      return fail(ENGRAM_EINVAL, "hidden, kv and wqk must be 16-byte aligned");
+    if (!aligned(tok, 4) || !aligned(gate_out, 4)) return fail(ENGRAM_EINVAL, "tok/gate_out misaligned");
+  }
+  return ENGRAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,30 +259,16 @@ int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
 
 int engram_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t H, int32_t hc,
                    uint16_t* kv, hipStream_t stream) {
-  int rc = check_dims(H, hc);
+  const int rc = check_project_args(mem, T, wkv, H, hc, kv);
   if (rc != ENGRAM_OK) return rc;
-  if (T < 0 || T > (int64_t)INT32_MAX) return fail(ENGRAM_EINVAL, "T out of range");
-  if (T > 0) {
-    if (!mem || !wkv || !kv) return fail(ENGRAM_EINVAL, "NULL pointer");
-    if (!aligned(mem, 16) || !aligned(wkv, 16) || !aligned(kv, 16))
-      return fail(ENGRAM_EINVAL, "mem, wkv and kv must be 16-byte aligned");
-  }
   return from_hip(engram::launch_project(mem, T, wkv, (hc + 1) * H, kv, stream), "engram_project");
 }
 
 int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const uint32_t* tok,
                 int64_t T, int32_t H, int32_t hc, float eps, float dot_scale, float* gate_out,
                 hipStream_t stream) {
-  int rc = check_dims(H, hc);
+  const int rc = check_gate_args(hidden, kv, wqk, tok, T, H, hc, eps, gate_out);
   if (rc != ENGRAM_OK) return rc;
-  if (T < 0 || T > (int64_t)INT32_MAX) return fail(ENGRAM_EINVAL, "T out of range");
-  if (!(eps >= 0.0f)) return fail(ENGRAM_EINVAL, "eps must be >= 0");
-  if (T > 0) {
-    if (!hidden || !kv || !wqk) return fail(ENGRAM_EINVAL, "NULL pointer");
-    if (!aligned(hidden, 16) || !aligned(kv, 16) || !aligned(wqk, 16))
-      return fail(ENGRAM_EINVAL, "hidden, kv and wqk must be 16-byte aligned");
-    if (!aligned(tok, 4) || !aligned(gate_out, 4)) return fail(ENGRAM_EINVAL, "tok/gate_out misaligned");
-  }
   return from_hip(engram::launch_gate(hidden, kv, wqk, tok, T, H, hc, eps, dot_scale, gate_out, stream),
                   "engram_gate");
 }
@@ -284,6 +300,12 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
   uint16_t* mem = reinterpret_cast<uint16_t*>(w + round256(t * ENGRAM_BUCKETS * 4));
   uint16_t* kv = reinterpret_cast<uint16_t*>(w + round256(t * ENGRAM_BUCKETS * 4) +
                                              round256(t * ENGRAM_MEM * 2));
+  // Every stage's arguments are checked before anything is enqueued.
+  if ((rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx)) != ENGRAM_OK ||
+      (rc = check_gather_args(idx, T, codes, scales, params->n_rows, mem)) != ENGRAM_OK ||
+      (rc = check_project_args(mem, T, wkv, H, hc, kv)) != ENGRAM_OK ||
+      (rc = check_gate_args(hidden, kv, wqk, tok, T, H, hc, eps, gate_out)) != ENGRAM_OK)
+    return rc;
   auto mark = [&](int i) -> int {
     if (stage_events == nullptr) return ENGRAM_OK;
     return from_hip(hipEventRecord(stage_events[i], stream), "engram_forward: hipEventRecord");
@@ -292,10 +314,6 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
   if (T <= engram::kHashGatherMaxTokens && S <= engram::kHashGatherMaxSeqs) {
     // Small batch: one kernel hashes, gathers and decodes; stage events 1
     // and 2 both mark its end.
-    rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx);
-    if (rc != ENGRAM_OK) return rc;
-    rc = check_gather_args(idx, T, codes, scales, params->n_rows, mem);
-    if (rc != ENGRAM_OK) return rc;
     if (T > 0) {
       rc = from_hip(engram::launch_hash_gather(tok, cu_seqlens, S, T, hist, token_map, map_len,
                                                *params, codes, scales, idx, mem, err_flags, stream),
@@ -304,17 +322,22 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
     }
     if ((rc = mark(1)) != ENGRAM_OK) return rc;
   } else {
-    rc = engram_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx, err_flags, stream);
+    rc = from_hip(engram::launch_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, idx,
+                                      err_flags, stream),
+                  "engram_forward: hash");
     if (rc != ENGRAM_OK) return rc;
     if ((rc = mark(1)) != ENGRAM_OK) return rc;
-    rc = engram_gather_decode(idx, T, codes, scales, params->n_rows, mem, err_flags, stream);
+    rc = from_hip(engram::launch_gather_decode(idx, T, codes, scales, params->n_rows, mem, err_flags,
+                                               stream),
+                  "engram_forward: gather + decode");
     if (rc != ENGRAM_OK) return rc;
   }
   if ((rc = mark(2)) != ENGRAM_OK) return rc;
-  rc = engram_project(mem, T, wkv, H, hc, kv, stream);
+  rc = from_hip(engram::launch_project(mem, T, wkv, (hc + 1) * H, kv, stream), "engram_forward: project");
   if (rc != ENGRAM_OK) return rc;
   if ((rc = mark(3)) != ENGRAM_OK) return rc;
-  rc = engram_gate(hidden, kv, wqk, tok, T, H, hc, eps, dot_scale, gate_out, stream);
+  rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, T, H, hc, eps, dot_scale, gate_out, stream),
+                "engram_forward: gate");
   if (rc != ENGRAM_OK) return rc;
   return mark(4);
 }

@@ -192,7 +192,9 @@ size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
 /* One Engram layer: engram_hash -> engram_gather_decode -> engram_project ->
  * engram_gate, enqueued on one stream, intermediates in `ws` (caller-owned
  * device memory of at least engram_forward_workspace(T, H, hc) bytes,
- * 256-byte aligned). Arguments mean what they mean in the stage calls.
+ * 256-byte aligned). Arguments mean what they mean in the stage calls, and
+ * every stage's host checks run before anything is enqueued (an
+ * ENGRAM_EINVAL return leaves the stream untouched).
  * Per step: call once per layer with that layer's params/table/wkv/wqk and
  * hidden, all reading the same `hist`, then engram_history_append once.
  * For T <= 1024 tokens in S <= 1024 sequences (decode steps) hashing,

@@ -130,6 +130,34 @@ def test_stage_entry_points_reject_bad_shapes_before_launch(E):
     assert L.engram_project(None, 0, None, 256, 4, None, None) == 0
 
 
+def test_forward_checks_its_stage_arguments_on_both_paths(E):
+    """engram_forward runs hash + gather as one kernel for T <= 1,024 tokens in
+    S <= 1,024 sequences and as two kernels otherwise; either way it applies
+    engram_hash's and engram_gather_decode's host checks before any launch."""
+    L = E.lib
+    p, _ = _params()
+    fake = ctypes.c_void_p(0x10000)
+    H, hc = 256, 4
+    for S, T in ((1, 8), (1, 2000), (1500, 1500)):
+        need = L.engram_forward_workspace(T, H, hc)
+        ws = ctypes.c_void_p(0x100000)   # 256-byte aligned, never dereferenced
+        def fwd(hp, codes=fake, scales=fake, tmap_len=10):
+            return L.engram_forward(fake, fake, S, T, fake, fake, tmap_len, ctypes.byref(hp), codes,
+                                    scales, fake, fake, fake, H, hc, 1e-6, 1.0, ws, need, None, None,
+                                    None, None)
+        bad = E.HashParams.from_any(p)
+        bad.prime[0] = 4
+        assert fwd(bad) == -1, (S, T)
+        hp = E.HashParams.from_any(p)
+        assert fwd(hp, codes=ctypes.c_void_p(0x10008)) == -1, (S, T)     # codes not 16-byte aligned
+        assert b"alignment" in L.engram_last_error()
+        assert fwd(hp, tmap_len=0) == -1, (S, T)                         # empty token map
+    # no tokens: nothing to launch, succeeds without a device
+    hp = E.HashParams.from_any(p)
+    assert L.engram_forward(None, fake, 1, 0, None, None, 0, ctypes.byref(hp), None, None, None,
+                            None, None, H, hc, 1e-6, 1.0, None, 0, None, None, None, None) == 0
+
+
 def test_workspace_size_formula(E):
     T, H, hc = 1000, 5120, 4
     r = lambda x: (x + 255) // 256 * 256
