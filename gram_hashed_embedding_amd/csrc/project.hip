@@ -54,8 +54,9 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // has two whole K steps (~4,000 cycles) to return. Loads use buffer
 // instructions whose row offsets sit in per-chunk registers and whose K
 // position is a scalar offset. Each K step is cut into four K16 steps; the
-// loads, LDS writes and next fragment reads are spread between the MFMAs of
-// the first three, and one barrier, before the last, publishes tile kt+1.
+// loads and LDS writes are spread between the MFMAs of the first three, every
+// K16 step reads the next one's fragments first, and one barrier, before the
+// last, publishes tile kt+1.
 //
 // LDS rows are 128 bytes (64 bf16 of K); 16-byte chunk c of row r is stored
 // in slot c ^ swz(r), which keeps the 32-row fragment reads free of bank
@@ -104,18 +105,28 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Order inside one K16 step: 16 MFMAs with the LDS writes on the even MFMA
-// slots, the global loads on the odd ones and the NR fragment reads in the
-// back half; nothing crosses the step. Spacing the 16-byte LDS writes keeps
-// the LDS write-data queue from filling, which would stall MFMA issue.
+// Order inside one K16 step: 16 MFMAs; the NR fragment reads for the next
+// K16 step go first, two per MFMA slot, then from slot 5 on the LDS writes and
+// the global loads alternate (writes on odd slots, loads on even ones);
+// nothing crosses the step. LDS returns a wave's operations in order, so a
+// fragment read issued behind this step's 16-byte writes waits for them: with
+// the reads in the back half, the next step's first MFMAs stalled on reads
+// queued behind writes, and reads first is 4-6% faster on the 50,032 x 25,600
+// x 6,144 projection (interleaved A/B runs on three boxes; four or eight reads
+// per slot, or writes from slot 2 or 3, measured slower). Spacing the writes
+// keeps the LDS write-data queue from filling, which would stall MFMA issue.
 template <int NW, int NV, int NR>
 __device__ __forceinline__ void wt_interleave() {
+  constexpr int kFirstWrite = 5;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               // MFMA
-    if ((q & 1) == 0 && q / 2 < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
-    if ((q & 1) == 1 && q / 2 < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
-    if (q >= 16 - NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // DS read
+    if (q < NR / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);               // DS read x 2
+    if (q >= kFirstWrite) {
+      const int o = q - kFirstWrite;
+      if ((o & 1) == 0 && o / 2 < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
+      if ((o & 1) == 1 && o / 2 < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
