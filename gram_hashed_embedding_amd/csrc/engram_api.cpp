@@ -253,7 +253,8 @@ int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                          uint32_t* err_flags, hipStream_t stream) {
   const int rc = check_gather_args(idx, T, codes, scales, n_rows, mem);
   if (rc != ENGRAM_OK) return rc;
-  return from_hip(engram::launch_gather_decode(idx, T, codes, scales, n_rows, mem, err_flags, stream),
+  return from_hip(engram::launch_gather_decode(idx, T, codes, scales, n_rows, mem, nullptr, err_flags,
+                                                stream),
                   "engram_gather_decode");
 }
 
@@ -261,7 +262,8 @@ int engram_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t 
                    uint16_t* kv, hipStream_t stream) {
   const int rc = check_project_args(mem, T, wkv, H, hc, kv);
   if (rc != ENGRAM_OK) return rc;
-  return from_hip(engram::launch_project(mem, T, wkv, (hc + 1) * H, kv, stream), "engram_project");
+  return from_hip(engram::launch_project(mem, T, nullptr, wkv, (hc + 1) * H, kv, stream),
+                  "engram_project");
 }
 
 int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const uint32_t* tok,
@@ -269,14 +271,16 @@ int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const ui
                 hipStream_t stream) {
   const int rc = check_gate_args(hidden, kv, wqk, tok, T, H, hc, eps, gate_out);
   if (rc != ENGRAM_OK) return rc;
-  return from_hip(engram::launch_gate(hidden, kv, wqk, tok, T, H, hc, eps, dot_scale, gate_out, stream),
+  return from_hip(engram::launch_gate(hidden, kv, wqk, tok, nullptr, T, H, hc, eps, dot_scale, gate_out,
+                                      stream),
                   "engram_gate");
 }
 
 size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc) {
   if (T <= 0 || H <= 0 || hc <= 0) return 0;
   const size_t t = (size_t)T;
-  return round256(t * ENGRAM_BUCKETS * 4) + round256(t * ENGRAM_MEM * 2) +
+  return round256(t * ENGRAM_BUCKETS * 4) + round256(t * 4) +
+         round256(4 * (1 + (size_t)engram::live_chunks(T))) + round256(t * ENGRAM_MEM * 2) +
          round256(t * (size_t)(hc + 1) * (size_t)H * 2);
 }
 
@@ -294,12 +298,18 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
       return fail(ENGRAM_EINVAL, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
     if (!aligned(ws, 256)) return fail(ENGRAM_EINVAL, "workspace must be 256-byte aligned");
   }
+  // Workspace: idx [T][24] | slot [T] | live count + per-chunk counts |
+  // mem | kv, each section 256-byte aligned.
   uint8_t* w = static_cast<uint8_t*>(ws);
   const size_t t = T > 0 ? (size_t)T : 0;
+  const size_t o_slot = round256(t * ENGRAM_BUCKETS * 4), o_count = o_slot + round256(t * 4);
+  const size_t o_mem = o_count + round256(4 * (1 + (size_t)engram::live_chunks((int64_t)t)));
+  const size_t o_kv = o_mem + round256(t * ENGRAM_MEM * 2);
   uint32_t* idx = reinterpret_cast<uint32_t*>(w);
-  uint16_t* mem = reinterpret_cast<uint16_t*>(w + round256(t * ENGRAM_BUCKETS * 4));
-  uint16_t* kv = reinterpret_cast<uint16_t*>(w + round256(t * ENGRAM_BUCKETS * 4) +
-                                             round256(t * ENGRAM_MEM * 2));
+  uint32_t* slot = reinterpret_cast<uint32_t*>(w + o_slot);
+  uint32_t* live = reinterpret_cast<uint32_t*>(w + o_count);
+  uint16_t* mem = reinterpret_cast<uint16_t*>(w + o_mem);
+  uint16_t* kv = reinterpret_cast<uint16_t*>(w + o_kv);
   // Every stage's arguments are checked before anything is enqueued.
   if ((rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx)) != ENGRAM_OK ||
       (rc = check_gather_args(idx, T, codes, scales, params->n_rows, mem)) != ENGRAM_OK ||
@@ -311,7 +321,7 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
     return from_hip(hipEventRecord(stage_events[i], stream), "engram_forward: hipEventRecord");
   };
   if ((rc = mark(0)) != ENGRAM_OK) return rc;
-  if (T <= engram::kHashGatherMaxTokens && S <= engram::kHashGatherMaxSeqs) {
+  if (T == 0 || (T <= engram::kHashGatherMaxTokens && S <= engram::kHashGatherMaxSeqs)) {
     // Small batch: one kernel hashes, gathers and decodes; stage events 1
     // and 2 both mark its end.
     if (T > 0) {
@@ -321,22 +331,40 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
       if (rc != ENGRAM_OK) return rc;
     }
     if ((rc = mark(1)) != ENGRAM_OK) return rc;
-  } else {
-    rc = from_hip(engram::launch_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, idx,
-                                      err_flags, stream),
-                  "engram_forward: hash");
+    if ((rc = mark(2)) != ENGRAM_OK) return rc;
+    rc = from_hip(engram::launch_project(mem, T, nullptr, wkv, (hc + 1) * H, kv, stream),
+                  "engram_forward: project");
     if (rc != ENGRAM_OK) return rc;
-    if ((rc = mark(1)) != ENGRAM_OK) return rc;
-    rc = from_hip(engram::launch_gather_decode(idx, T, codes, scales, params->n_rows, mem, err_flags,
-                                               stream),
-                  "engram_forward: gather + decode");
+    if ((rc = mark(3)) != ENGRAM_OK) return rc;
+    rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, nullptr, T, H, hc, eps, dot_scale,
+                                      gate_out, stream),
+                  "engram_forward: gate");
     if (rc != ENGRAM_OK) return rc;
+    return mark(4);
   }
+  // Larger batches: only live (non-DEAD) positions are decoded and projected.
+  // DEAD positions pass through the gate untouched, so their k/v are never
+  // read; the live rows of mem and kv are packed in position order, slot[t]
+  // locating position t's, and the projection reads the live count on the
+  // device, so nothing waits on the host.
+  rc = from_hip(engram::launch_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, idx,
+                                    err_flags, stream),
+                "engram_forward: hash");
+  if (rc != ENGRAM_OK) return rc;
+  rc = from_hip(engram::launch_live_slots(tok, T, slot, live, live + 1, stream), "engram_forward: live slots");
+  if (rc != ENGRAM_OK) return rc;
+  if ((rc = mark(1)) != ENGRAM_OK) return rc;
+  rc = from_hip(engram::launch_gather_decode(idx, T, codes, scales, params->n_rows, mem, slot,
+                                             err_flags, stream),
+                "engram_forward: gather + decode");
+  if (rc != ENGRAM_OK) return rc;
   if ((rc = mark(2)) != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_project(mem, T, wkv, (hc + 1) * H, kv, stream), "engram_forward: project");
+  rc = from_hip(engram::launch_project(mem, T, live, wkv, (hc + 1) * H, kv, stream),
+                "engram_forward: project");
   if (rc != ENGRAM_OK) return rc;
   if ((rc = mark(3)) != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, T, H, hc, eps, dot_scale, gate_out, stream),
+  rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, slot, T, H, hc, eps, dot_scale, gate_out,
+                                    stream),
                 "engram_forward: gate");
   if (rc != ENGRAM_OK) return rc;
   return mark(4);

@@ -22,9 +22,18 @@ hipError_t launch_hash(const uint32_t* tok, const int32_t* cu, int32_t S, int64_
                        const uint32_t* hist, const uint32_t* map, uint32_t map_len,
                        const engram_hash_params& p, uint32_t* idx, uint32_t* err,
                        hipStream_t st);
+// Rows of the live (non-DEAD) positions of tok[T]: slot[t] = live positions
+// before t (ENGRAM_DEAD_IDX for a DEAD one), *count = live positions.
+// chunk_count: scratch of live_chunks(T) words.
+constexpr int64_t kLiveChunkPositions = 4096;
+inline int64_t live_chunks(int64_t T) { return (T + kLiveChunkPositions - 1) / kLiveChunkPositions; }
+hipError_t launch_live_slots(const uint32_t* tok, int64_t T, uint32_t* slot, uint32_t* count,
+                             uint32_t* chunk_count, hipStream_t st);
+// slot: NULL (position t's rows go to mem row t), or the live_slots map
+// (they go to row slot[t]; DEAD positions write nothing).
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                                 const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
-                                uint32_t* err, hipStream_t st);
+                                const uint32_t* slot, uint32_t* err, hipStream_t st);
 // Hash, gather and decode as one kernel (hash_gather.hip): for batches of at
 // most kHashGatherMaxTokens tokens in at most kHashGatherMaxSeqs sequences,
 // where both steps are latency-bound chains of loads. Writes the same idx and
@@ -36,11 +45,14 @@ hipError_t launch_hash_gather(const uint32_t* tok, const int32_t* cu, int32_t S,
                               const engram_hash_params& p, const uint8_t* codes,
                               const uint8_t* scales, uint32_t* idx, uint16_t* mem, uint32_t* err,
                               hipStream_t st);
-hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
-                          uint16_t* kv, hipStream_t st);
+// live_rows: NULL, or a device word holding how many of the T rows of mem
+// count (T > 256 only; rows past it are neither computed in full nor stored).
+hipError_t launch_project(const uint16_t* mem, int64_t T, const uint32_t* live_rows,
+                          const uint16_t* wkv, int32_t N, uint16_t* kv, hipStream_t st);
+// kv_row: NULL (position t reads kv row t), or the live_slots map.
 hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
-                       const uint32_t* tok, int64_t T, int32_t H, int32_t hc, float eps,
-                       float dot_scale, float* gate_out, hipStream_t st);
+                       const uint32_t* tok, const uint32_t* kv_row, int64_t T, int32_t H,
+                       int32_t hc, float eps, float dot_scale, float* gate_out, hipStream_t st);
 hipError_t launch_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin,
                             uint64_t n_rows, uint64_t key_data, uint64_t key_scale,
                             hipStream_t st);

@@ -100,11 +100,14 @@ __device__ __forceinline__ void nt_store(uint16_t* p, uint32_t a, uint32_t b, ui
 // the waits at the joins drained the queue. A DEAD token, or a position past
 // the end, reads the norm-weight array instead (80 KB that stay in L2), so it
 // moves no HBM bytes; its sums are discarded and its hidden is not stored.
+//
+// kv_row, when given, maps a position to its row of kv (the projection then
+// ran over the live positions only); otherwise position t reads row t.
 template <int HC, int THREADS>
 __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
     uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
-    const uint32_t* __restrict__ tok, int64_t T, float eps, float dot_scale,
-    float* __restrict__ gate_out) {
+    const uint32_t* __restrict__ tok, const uint32_t* __restrict__ kv_row, int64_t T, float eps,
+    float dot_scale, float* __restrict__ gate_out) {
   constexpr int WAVES = THREADS / 64;
   constexpr int H = THREADS * 8;
   static_assert((HC + 1) * H * 2 <= HC * H * 4, "stand-in rows must fit in the norm weights");
@@ -114,39 +117,49 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
   const uint16_t* stand_in = reinterpret_cast<const uint16_t*>(wqk);
   uint4 hq[HC], kq[HC], vq;
   const int64_t G = gridDim.x;
-  auto load_k = [&](int64_t tt, bool l) {
-    const uint16_t* kv_t = (l ? kv + tt * (int64_t)(HC + 1) * H : stand_in) + tid * 8;
+  auto load_k = [&](int64_t kr, bool l) {
+    const uint16_t* kv_t = (l ? kv + kr * (int64_t)(HC + 1) * H : stand_in) + tid * 8;
 #pragma unroll
     for (int b = 0; b < HC; ++b) kq[b] = nt_load(kv_t + b * H);
   };
-  auto load_hv = [&](int64_t tt, bool l) {
-    const uint16_t* kv_t = (l ? kv + tt * (int64_t)(HC + 1) * H : stand_in) + tid * 8;
+  auto load_hv = [&](int64_t tt, int64_t kr, bool l) {
+    const uint16_t* kv_t = (l ? kv + kr * (int64_t)(HC + 1) * H : stand_in) + tid * 8;
     const uint16_t* h_t = (l ? hidden + tt * (int64_t)HC * H : stand_in) + tid * 8;
     vq = nt_load(kv_t + HC * H);
 #pragma unroll
     for (int b = 0; b < HC; ++b) hq[b] = nt_load(h_t + b * H);
   };
-  // Liveness of this workgroup's tokens, 64 at a time: lane i of `flags`
-  // holds token blockIdx.x + (k0 + i) * G (0 past the end).
+  // Liveness and kv row of this workgroup's tokens, 64 at a time: lane i of
+  // `flags` and `rows` holds token blockIdx.x + (k0 + i) * G (0 past the end).
   const int lane = tid & 63;
-  auto load_flags = [&](int64_t k0) -> uint32_t {
+  uint32_t flags = 0, rows = 0;
+  auto load_meta = [&](int64_t k0) {
     const int64_t tt = blockIdx.x + (k0 + lane) * G;
-    return (tt < T && (tok == nullptr || tok[tt] != ENGRAM_DEAD_TOKEN)) ? 1u : 0u;
+    const bool in = tt < T;
+    flags = (in && (tok == nullptr || tok[tt] != ENGRAM_DEAD_TOKEN)) ? 1u : 0u;
+    // (clamped: a DEAD position's map entry is never used, and no entry may
+    // leave kv)
+    rows = kv_row == nullptr ? (uint32_t)tt : (in ? min(kv_row[tt], (uint32_t)(T - 1)) : 0u);
   };
-  uint32_t flags = load_flags(0);
+  load_meta(0);
   auto live_at = [&](int64_t it) -> bool {
     return __builtin_amdgcn_readlane(flags, (int)(it & 63)) != 0;
+  };
+  auto row_at = [&](int64_t it) -> int64_t {
+    return (int64_t)(uint32_t)__builtin_amdgcn_readlane(rows, (int)(it & 63));
   };
 
   int64_t it = 0, t = blockIdx.x;
   bool lv = live_at(0);
   bool lvn = live_at(1);
-  load_hv(t, lv);
-  load_k(t, lv);
+  int64_t kr = row_at(0), krn = row_at(1);
+  load_hv(t, kr, lv);
+  load_k(kr, lv);
   for (; t < T; t += G, ++it) {
     const int64_t tn = t + G;
-    if (((it + 2) & 63) == 0) flags = load_flags(it + 2);
+    if (((it + 2) & 63) == 0) load_meta(it + 2);
     const bool lvnn = live_at(it + 2);
+    const int64_t krnn = row_at(it + 2);
     float s[3 * HC];
 #pragma unroll
     for (int b = 0; b < HC; ++b) {
@@ -164,7 +177,7 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
         s[3 * b + 2] = fmaf(h[i] * k[i], w[i], s[3 * b + 2]);
       }
     }
-    load_k(tn, lvn);
+    load_k(krn, lvn);
     reduce_gates<HC, WAVES>(s, red, g_sh, H, eps, dot_scale, lv ? gate_out : nullptr, t);
     if (lv) {
       float v[8];
@@ -185,9 +198,10 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
     } else if (gate_out != nullptr && tid < HC) {
       gate_out[t * HC + tid] = 0.0f;
     }
-    load_hv(tn, lvn);
+    load_hv(tn, krn, lvn);
     lv = lvn;
     lvn = lvnn;
+    krn = krnn;
     __syncthreads();   // keeps the waves of the workgroup on the same token
   }
 }
@@ -201,8 +215,8 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void gate_branch_kernel(
     uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
-    const uint32_t* __restrict__ tok, int hc, float eps, float dot_scale,
-    float* __restrict__ gate_out) {
+    const uint32_t* __restrict__ tok, const uint32_t* __restrict__ kv_row, int hc, float eps,
+    float dot_scale, float* __restrict__ gate_out) {
   constexpr int WAVES = THREADS / 64;
   constexpr int H = THREADS * 8;
   const int64_t t = blockIdx.x / hc;
@@ -213,7 +227,9 @@ __global__ __launch_bounds__(THREADS) void gate_branch_kernel(
     return;
   }
   uint16_t* h_t = hidden + (t * hc + b) * (int64_t)H + tid * 8;
-  const uint16_t* kv_t = kv + t * (int64_t)(hc + 1) * H + tid * 8;
+  const int64_t T = gridDim.x / hc;
+  const int64_t kr = kv_row == nullptr ? t : (int64_t)min(kv_row[t], (uint32_t)(T - 1));
+  const uint16_t* kv_t = kv + kr * (int64_t)(hc + 1) * H + tid * 8;
   const uint4 hq = nt_load(h_t);
   const uint4 kq = nt_load(kv_t + b * H);
   const uint4 vq = nt_load(kv_t + hc * H);
@@ -250,8 +266,8 @@ __global__ __launch_bounds__(THREADS) void gate_branch_kernel(
 constexpr int kGenThreads = 256;
 __global__ __launch_bounds__(kGenThreads) void gate_generic_kernel(
     uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
-    const uint32_t* __restrict__ tok, int H, int hc, float eps, float dot_scale,
-    float* __restrict__ gate_out) {
+    const uint32_t* __restrict__ tok, const uint32_t* __restrict__ kv_row, int H, int hc, float eps,
+    float dot_scale, float* __restrict__ gate_out) {
   constexpr int WAVES = kGenThreads / 64;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -261,7 +277,8 @@ __global__ __launch_bounds__(kGenThreads) void gate_generic_kernel(
   }
   const int chunks = H / 8;
   uint16_t* h_t = hidden + t * (int64_t)hc * H;
-  const uint16_t* kv_t = kv + t * (int64_t)(hc + 1) * H;
+  const int64_t kr = kv_row == nullptr ? t : (int64_t)min(kv_row[t], (uint32_t)(gridDim.x - 1));
+  const uint16_t* kv_t = kv + kr * (int64_t)(hc + 1) * H;
   float s[3 * kMaxHc];
 #pragma unroll
   for (int q = 0; q < 3 * kMaxHc; ++q) s[q] = 0.0f;
@@ -330,8 +347,8 @@ __global__ __launch_bounds__(kGenThreads) void gate_generic_kernel(
 }  // namespace
 
 hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
-                       const uint32_t* tok, int64_t T, int32_t H, int32_t hc, float eps,
-                       float dot_scale, float* gate_out, hipStream_t st) {
+                       const uint32_t* tok, const uint32_t* kv_row, int64_t T, int32_t H,
+                       int32_t hc, float eps, float dot_scale, float* gate_out, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (H == 5120) {
     int n_cu = 0;
@@ -339,21 +356,21 @@ hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
     if (e != hipSuccess) return e;
     if ((hc != 4 || T * hc <= 4 * (int64_t)n_cu) && T * hc <= (int64_t)INT32_MAX) {
       // decode-sized batches (and other branch counts): a workgroup per (token, branch)
-      gate_branch_kernel<640><<<(unsigned)(T * hc), 640, 0, st>>>(hidden, kv, wqk, tok, hc, eps,
-                                                                  dot_scale, gate_out);
+      gate_branch_kernel<640><<<(unsigned)(T * hc), 640, 0, st>>>(hidden, kv, wqk, tok, kv_row, hc,
+                                                                  eps, dot_scale, gate_out);
       return hipGetLastError();
     }
     if (hc == 4) {
       // one resident workgroup per CU (the kernel keeps two tokens' loads in
       // registers, so a second workgroup would not fit beside it)
       const unsigned grid = (unsigned)(T < n_cu ? T : n_cu);
-      gate_stream_kernel<4, 640><<<grid, 640, 0, st>>>(hidden, kv, wqk, tok, T, eps, dot_scale,
-                                                       gate_out);
+      gate_stream_kernel<4, 640><<<grid, 640, 0, st>>>(hidden, kv, wqk, tok, kv_row, T, eps,
+                                                       dot_scale, gate_out);
       return hipGetLastError();
     }
   }
-  gate_generic_kernel<<<(unsigned)T, kGenThreads, 0, st>>>(hidden, kv, wqk, tok, H, hc, eps,
-                                                           dot_scale, gate_out);
+  gate_generic_kernel<<<(unsigned)T, kGenThreads, 0, st>>>(hidden, kv, wqk, tok, kv_row, H, hc,
+                                                           eps, dot_scale, gate_out);
   return hipGetLastError();
 }
 

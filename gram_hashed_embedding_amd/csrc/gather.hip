@@ -24,10 +24,12 @@ constexpr int kBlock = 256;
 constexpr int kGroups = kBlock / 16;     // rows per pass of one workgroup
 constexpr int kRowsInFlight = 4;         // passes per workgroup (rows per lane)
 
+// With `slot` (from live_slots_kernel), position t's rows go to row slot[t]
+// of mem and a DEAD position writes nothing; without it, to row t.
 __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
     const uint32_t* __restrict__ idx, int64_t total_rows, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, uint64_t n_rows, uint16_t* __restrict__ mem,
-    uint32_t* err) {
+    const uint32_t* __restrict__ slot, uint32_t* err) {
   const int l = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;
   const int64_t base = (int64_t)blockIdx.x * (kGroups * kRowsInFlight);
@@ -37,6 +39,7 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
   const int sh = 8 * (l >> 2);
   uint2 ca[kRowsInFlight], cb[kRowsInFlight];
   uint32_t sa[kRowsInFlight], sb[kRowsInFlight];
+  int64_t out_row[kRowsInFlight];   // destination row of mem, or -1 for none
   bool live[kRowsInFlight];
 #pragma unroll
   for (int u = 0; u < kRowsInFlight; ++u) {
@@ -44,7 +47,15 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
     live[u] = false;
     ca[u] = cb[u] = make_uint2(0, 0);
     sa[u] = sb[u] = 127;
+    out_row[u] = -1;
     if (r < total_rows) {
+      if (slot == nullptr) {
+        out_row[u] = r;
+      } else {
+        const int64_t t = r / ENGRAM_BUCKETS;
+        const uint32_t st = slot[t];
+        if (st != ENGRAM_DEAD_IDX) out_row[u] = (int64_t)st * ENGRAM_BUCKETS + (r - t * ENGRAM_BUCKETS);
+      }
       const uint32_t row = idx[r];
       if (row != ENGRAM_DEAD_IDX) {
         if ((uint64_t)row < n_rows) {
@@ -63,9 +74,8 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
   }
 #pragma unroll
   for (int u = 0; u < kRowsInFlight; ++u) {
-    const int64_t r = base + u * kGroups + grp;
-    if (r >= total_rows) continue;
-    decode_store_row(mem + r * ENGRAM_ROW, l, live[u], ca[u], cb[u], sa[u], sb[u]);
+    if (out_row[u] < 0) continue;
+    decode_store_row(mem + out_row[u] * ENGRAM_ROW, l, live[u], ca[u], cb[u], sa[u], sb[u]);
   }
 }
 
@@ -73,12 +83,12 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
 
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                                 const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
-                                uint32_t* err, hipStream_t st) {
+                                const uint32_t* slot, uint32_t* err, hipStream_t st) {
   const int64_t rows = T * ENGRAM_BUCKETS;
   if (rows == 0) return hipSuccess;
   const int64_t per_block = (int64_t)kGroups * kRowsInFlight;
   const unsigned blocks = (unsigned)((rows + per_block - 1) / per_block);
-  gather_decode_kernel<<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, mem, err);
+  gather_decode_kernel<<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, mem, slot, err);
   return hipGetLastError();
 }
 

@@ -65,6 +65,82 @@ __global__ __launch_bounds__(kBlock) void history_fill_kernel(uint32_t* __restri
   if (i < n) dst[i] = src ? src[i] : value;
 }
 
+// Rows of the live (non-DEAD) positions: slot[t] = number of live positions
+// before t, or ENGRAM_DEAD_IDX for a DEAD one, and *count = number of live
+// positions. Two passes over chunks of kLiveChunk positions (kLivePer
+// consecutive ones per thread): live_count_kernel counts each chunk's live
+// positions, then live_slots_kernel adds up the counts of the chunks before
+// its own (at most a few hundred) and scans its chunk (wave shuffles, then
+// the wave totals). Both passes spread over the whole GPU.
+constexpr int kLiveThreads = 256, kLivePer = 16, kLiveChunk = kLiveThreads * kLivePer;
+static_assert(kLiveChunk == kLiveChunkPositions, "chunk size");
+
+__device__ __forceinline__ uint32_t live_bits(const uint32_t* __restrict__ tok, int64_t T, int64_t t0) {
+  uint32_t live = 0;    // bit i: position t0 + i is live
+#pragma unroll
+  for (int i = 0; i < kLivePer; ++i)
+    if (t0 + i < T && tok[t0 + i] != ENGRAM_DEAD_TOKEN) live |= 1u << i;
+  return live;
+}
+
+template <int WAVES>
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) total += sh[w];
+  return total;
+}
+
+__global__ __launch_bounds__(kLiveThreads) void live_count_kernel(const uint32_t* __restrict__ tok,
+                                                                  int64_t T, uint32_t* __restrict__ chunk_count) {
+  __shared__ uint32_t sh[kLiveThreads / 64];
+  const int64_t t0 = (int64_t)blockIdx.x * kLiveChunk + (int64_t)threadIdx.x * kLivePer;
+  const uint32_t total = block_sum<kLiveThreads / 64>((uint32_t)__builtin_popcount(live_bits(tok, T, t0)), sh);
+  if (threadIdx.x == 0) chunk_count[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kLiveThreads) void live_slots_kernel(const uint32_t* __restrict__ tok,
+                                                                  int64_t T,
+                                                                  const uint32_t* __restrict__ chunk_count,
+                                                                  uint32_t* __restrict__ slot,
+                                                                  uint32_t* __restrict__ count) {
+  constexpr int WAVES = kLiveThreads / 64;
+  __shared__ uint32_t sh[WAVES], wave_tot[WAVES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // live positions in the chunks before this one
+  uint32_t before = 0;
+  for (int c = tid; c < (int)blockIdx.x; c += kLiveThreads) before += chunk_count[c];
+  before = block_sum<WAVES>(before, sh);
+  const int64_t t0 = (int64_t)blockIdx.x * kLiveChunk + (int64_t)tid * kLivePer;
+  const uint32_t live = live_bits(tok, T, t0);
+  const uint32_t c = (uint32_t)__builtin_popcount(live);
+  uint32_t incl = c;   // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t chunk_total = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    if (w < wave) before += wave_tot[w];
+    chunk_total += wave_tot[w];
+  }
+  uint32_t r = before + incl - c;
+#pragma unroll
+  for (int i = 0; i < kLivePer; ++i)
+    if (t0 + i < T) slot[t0 + i] = ((live >> i) & 1u) ? r++ : ENGRAM_DEAD_IDX;
+  if (blockIdx.x == gridDim.x - 1 && tid == WAVES * 64 - 1) *count = r;   // the last live row + 1
+  (void)chunk_total;
+}
+
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + kBlock - 1) / kBlock); }
 
 }  // namespace
@@ -89,6 +165,15 @@ hipError_t launch_history_append(uint32_t* hist, const uint32_t* tok, const int3
   if (S == 0) return hipSuccess;
   history_append_kernel<<<blocks_for(S), kBlock, 0, st>>>(hist, tok, cu, S, T, map, map_len,
                                                           pad_cid, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_live_slots(const uint32_t* tok, int64_t T, uint32_t* slot, uint32_t* count,
+                             uint32_t* chunk_count, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const unsigned chunks = (unsigned)((T + kLiveChunk - 1) / kLiveChunk);
+  live_count_kernel<<<chunks, kLiveThreads, 0, st>>>(tok, T, chunk_count);
+  live_slots_kernel<<<chunks, kLiveThreads, 0, st>>>(tok, T, chunk_count, slot, count);
   return hipGetLastError();
 }
 

@@ -134,10 +134,14 @@ __device__ __forceinline__ void wt_interleave() {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// live_rows, when given, holds the number of rows of A that count (M is then
+// only an upper bound from the host): tiles at or past it stop after their
+// first loads, and rows past it are not stored.
 __global__ __launch_bounds__(256) void wave_tile_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
-                                                        uint16_t* __restrict__ C, int M, int N,
-                                                        int m_tiles, int n_tiles) {
+                                                        uint16_t* __restrict__ C, int M,
+                                                        const uint32_t* __restrict__ live_rows,
+                                                        int N, int m_tiles, int n_tiles) {
   constexpr int BM = kWTBM, BN = kWTBN, ROWB = 128;
   constexpr int STAGE_A = BM * ROWB, STAGE = (BM + BN) * ROWB;
   constexpr int TM = 4, TN = 4;
@@ -147,6 +151,8 @@ __global__ __launch_bounds__(256) void wave_tile_kernel(const uint16_t* __restri
 
   int m0, n0;
   wt_tile_of(blockIdx.x, m_tiles, n_tiles, m0, n0);
+  // a scalar load; it has returned by the end of the prologue's first LDS wait
+  const int m_live = live_rows != nullptr ? (int)min(*live_rows, (uint32_t)M) : M;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -229,6 +235,10 @@ __global__ __launch_bounds__(256) void wave_tile_kernel(const uint16_t* __restri
   gload(1, 1, 0, 8);
   gload(0, 2, 0, 8);
   lds_barrier();
+  if (m0 >= m_live) {   // no live row in this tile (the same in every wave)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
   load_frags(0, 0, 0);
 
   // K step kt (LDS buffer kt & 1, register set (kt+1) & 1; the set is a
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(256) void wave_tile_kernel(const uint16_t* __restri
   for (int ch = tid; ch < BM * 32; ch += 256) {
     const int row = ch >> 5, cc = ch & 31;
     const int grow = m0 + row, gcol = n0 + cc * 8;
-    if (grow < M && gcol < N) {
+    if (grow < m_live && gcol < N) {
       const uint4 q = *reinterpret_cast<const uint4*>(lds + row * 512 + ((cc ^ (row & 15)) << 4));
       const u32x4 v = {q.x, q.y, q.z, q.w};
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (int64_t)grow * N + gcol));
@@ -461,18 +471,19 @@ hipError_t run_skinny(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32
   return hipGetLastError();
 }
 
-hipError_t run_wave_tile(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
-                         uint16_t* kv, hipStream_t st) {
+hipError_t run_wave_tile(const uint16_t* mem, int64_t T, const uint32_t* live_rows,
+                         const uint16_t* wkv, int32_t N, uint16_t* kv, hipStream_t st) {
   const int m_tiles = (int)((T + kWTBM - 1) / kWTBM);
   const int n_tiles = (N + kWTBN - 1) / kWTBN;
-  wave_tile_kernel<<<m_tiles * n_tiles, 256, 0, st>>>(mem, wkv, kv, (int)T, N, m_tiles, n_tiles);
+  wave_tile_kernel<<<m_tiles * n_tiles, 256, 0, st>>>(mem, wkv, kv, (int)T, live_rows, N, m_tiles,
+                                                      n_tiles);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N,
-                          uint16_t* kv, hipStream_t st) {
+hipError_t launch_project(const uint16_t* mem, int64_t T, const uint32_t* live_rows,
+                          const uint16_t* wkv, int32_t N, uint16_t* kv, hipStream_t st) {
   if (T == 0) return hipSuccess;
   // <MT, NC, R, U, SK> chosen by sweeps on the 25,600 x 6,144 wkv stream
   if (T <= 16) return run_skinny<1, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
@@ -481,7 +492,7 @@ hipError_t launch_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, i
   if (T <= 128) return run_skinny<8, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
   if (T <= 192) return run_skinny<12, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
   if (T <= 256) return run_skinny<16, 7, 3, 8, 64>(mem, T, wkv, N, kv, st);
-  return run_wave_tile(mem, T, wkv, N, kv, st);
+  return run_wave_tile(mem, T, live_rows, wkv, N, kv, st);
 }
 
 }  // namespace engram

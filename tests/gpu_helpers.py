@@ -124,10 +124,36 @@ def hidden_rows(cfg, layer: int, rows, batch: int = 0) -> np.ndarray:
 
 
 def workspace_views(ws: torch.Tensor, T: int, H: int, hc: int):
-    """(idx [T][24], mem [T][6144], kv [T][(hc+1)H]) host copies of engram_forward's workspace."""
+    """Device views (idx [T][24], slot [T], mem [T][6144], kv [T][(hc+1)H]) of
+    engram_forward's workspace: idx | slot | live counts | mem | kv,
+    each section 256-byte aligned. Batches of more than 1,024 tokens or
+    sequences pack the live (non-DEAD) positions' mem and kv rows in position
+    order (row slot[t] for position t); smaller ones keep row t for position t."""
     r = lambda x: (x + 255) // 256 * 256
-    nb, nm = r(T * 96), r(T * 12288)
+    o_slot = r(T * 96)
+    o_mem = o_slot + r(T * 4) + r(4 * (1 + (T + 4095) // 4096))
+    o_kv = o_mem + r(T * 12288)
     idx = ws[: T * 96].view(torch.int32)
-    mem = ws[nb: nb + T * 12288].view(torch.int16)
-    kv = ws[nb + nm: nb + nm + T * (hc + 1) * H * 2].view(torch.int16)
-    return idx, mem, kv
+    slot = ws[o_slot: o_slot + T * 4].view(torch.int32)
+    mem = ws[o_mem: o_mem + T * 12288].view(torch.int16)
+    kv = ws[o_kv: o_kv + T * (hc + 1) * H * 2].view(torch.int16)
+    return idx, slot, mem, kv
+
+
+def forward_rows(ws: torch.Tensor, T: int, S: int, H: int, hc: int, rows):
+    """Host copies of engram_forward's mem and kv rows for the given positions,
+    and a mask of the positions that have a row (all of them for small
+    batches; the live ones where rows are packed, whose DEAD positions have
+    none)."""
+    _, slot, mem, kv = workspace_views(ws, T, H, hc)
+    rows = np.asarray(rows, dtype=np.int64)
+    if T > 1024 or S > 1024:
+        sl = slot.cpu().numpy().view(np.uint32)[rows]
+        has = sl != 0xFFFFFFFF
+        src = np.where(has, sl, 0).astype(np.int64)
+    else:
+        has = np.ones(len(rows), dtype=bool)
+        src = rows
+    m = down16(mem).reshape(T, 6144)[src]
+    k = down16(kv).reshape(T, (hc + 1) * H)[src]
+    return m, k, has

@@ -161,7 +161,10 @@ def test_forward_checks_its_stage_arguments_on_both_paths(E):
 def test_workspace_size_formula(E):
     T, H, hc = 1000, 5120, 4
     r = lambda x: (x + 255) // 256 * 256
-    assert E.engram_forward_workspace(T, H, hc) == r(T * 96) + r(T * 12288) + r(T * 25600 * 2)
+    # idx | slot | live count and one count per 4,096 positions | mem | kv
+    for T in (1, 1000, 4096, 4097, 50032):
+        assert E.engram_forward_workspace(T, H, hc) == (r(T * 96) + r(T * 4) + r(4 * (1 + (T + 4095) // 4096))
+                                                        + r(T * 12288) + r(T * 25600 * 2))
     assert E.engram_forward_workspace(0, H, hc) == 0
 
 

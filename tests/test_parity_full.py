@@ -16,7 +16,7 @@ import engram_synth as synth
 from oracle import engram_oracle as O
 from tests.conftest import gpu_available
 from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, down32,
-                               hidden_device, hidden_rows, log, up16, up32, upf, workspace_views)
+                               forward_rows, hidden_device, hidden_rows, log, up16, up32, upf, workspace_views)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
@@ -47,14 +47,19 @@ def _layer_inputs(E, w, li):
     return dict(codes=codes, scales=scales, wkv=wkv, wkv_d=up16(wkv), wqk=wqk, wqk_d=upf(wqk))
 
 
-def _check_sampled(w, li, L, rows, idx_all, mem_d, kv_d, hid_in, hid_out, gate_d, dead):
-    """Oracle on sampled rows: decode from the oracle's indices, project, gate."""
+def _check_sampled(w, li, L, rows, idx_all, ws, T, S, hid_in, hid_out, gate_d, dead):
+    """Oracle on sampled rows: decode from the oracle's indices, project, gate.
+    mem and kv are compared where the position has a row (packed batches
+    skip DEAD positions, whose k/v the gate never reads)."""
     cfg, p = w.cfg, w.params[li]
     rows = np.asarray(sorted(set(int(r) for r in rows)))
     ref_mem = O.gather_decode(idx_all[rows], w.rows(li))
-    assert np.array_equal(down16(mem_d).reshape(-1, 6144)[rows], ref_mem)
+    got_mem, got_kv, has = forward_rows(ws, T, S, cfg.H, cfg.hc, rows)
+    assert np.all(has | dead[rows])
+    assert np.array_equal(got_mem[has], ref_mem[has])
     ref_kv = O.project(ref_mem, L["wkv"])
-    assert_bf16_close(down16(kv_d).reshape(-1, (cfg.hc + 1) * cfg.H)[rows], ref_kv, what="kv")
+    if has.any():
+        assert_bf16_close(got_kv[has], ref_kv[has], what="kv")
     new, g, dots = O.gate_residual(hid_in, ref_kv, L["wqk"], dead[rows], cfg.H, cfg.hc, 1e-6, 1.0)
     got_h = down16(hid_out).reshape(-1, cfg.hc, cfg.H)[rows]
     assert_bf16_close(got_h.reshape(-1, cfg.H), new.reshape(-1, cfg.H), what="hidden")
@@ -101,13 +106,14 @@ def test_full_size_one_layer(E):
     hid_in_rows = hidden_rows(cfg, 1, sorted(set(rows.tolist())))
     ws = torch.empty(E.engram_forward_workspace(T, cfg.H, cfg.hc), dtype=torch.uint8, device=DEV)
     gate_d = _forward(E, w, 0, L, up32(tok), up32(cu), up32(hist), up32(w.tmap), hidden_d, ws, T)
-    idx_d, mem_d, kv_d = workspace_views(ws, T, cfg.H, cfg.hc)
+    idx_d = workspace_views(ws, T, cfg.H, cfg.hc)[0]
     win, dead, _ = O.walk(tok, cu, hist, w.tmap, p.pad_cid)
     ref_idx = O.hash_windows(win, dead, p.mult, p.prime, p.offset)
     got_idx = down32(idx_d).reshape(T, 24)
     assert np.array_equal(got_idx, ref_idx)
     _ranges_ok(got_idx, dead, p)
-    n_small = _check_sampled(w, 0, L, rows, ref_idx, mem_d, kv_d, hid_in_rows, hidden_d, gate_d, dead)
+    n_small = _check_sampled(w, 0, L, rows, ref_idx, ws, T, len(cu) - 1, hid_in_rows, hidden_d, gate_d,
+                             dead)
     log(f"  sampled gates with |dot| < 1e-2: {n_small}")
 
 
@@ -134,12 +140,13 @@ def test_long_prefill_two_layers(E):
         hidden_d = hidden_device(cfg, cfg.layers[li], T)
         hid_in_rows = hidden_rows(cfg, cfg.layers[li], rows)
         gate_d = _forward(E, w, li, Ls[li], tok_d, cu_d, hist_d, tmap_d, hidden_d, ws, T)
-        idx_d, mem_d, kv_d = workspace_views(ws, T, cfg.H, cfg.hc)
+        idx_d = workspace_views(ws, T, cfg.H, cfg.hc)[0]
         ref_idx = O.hash_windows(win, dead, p.mult, p.prime, p.offset)
         got_idx = down32(idx_d).reshape(T, 24)
         assert np.array_equal(got_idx, ref_idx), f"layer {cfg.layers[li]}"
         _ranges_ok(got_idx, dead, p)
-        _check_sampled(w, li, Ls[li], rows, ref_idx, mem_d, kv_d, hid_in_rows, hidden_d, gate_d, dead)
+        _check_sampled(w, li, Ls[li], rows, ref_idx, ws, T, len(cu) - 1, hid_in_rows, hidden_d, gate_d,
+                       dead)
         del hidden_d
     # both layers read the same history; it is appended once, after them
     assert np.array_equal(down32(hist_d).reshape(1, 3), hist0)
@@ -193,7 +200,7 @@ def test_multimodal_batched_decode(E):
             rows = sorted(set(np.concatenate([edges[(edges >= 0) & (edges < Tc)],
                                               rng.integers(0, Tc, 6)]).tolist()))
             gate_d = _forward(E, w, li, Ls[li], tok_d, cu_d, hist_c, tmap_d, hidden_d, ws, Tc)
-            idx_d, mem_d, kv_d = workspace_views(ws, Tc, cfg.H, cfg.hc)
+            idx_d = workspace_views(ws, Tc, cfg.H, cfg.hc)[0]
             ref_idx = O.hash_windows(win, dead, p.mult, p.prime, p.offset)
             got_idx = down32(idx_d).reshape(Tc, 24)
             assert np.array_equal(got_idx, ref_idx), (c0, li)
@@ -201,7 +208,7 @@ def test_multimodal_batched_decode(E):
             if checked:
                 assert dead[rows].any() and (~dead[rows]).any()
                 hid_in_rows = hidden_rows(cfg, cfg.layers[li], np.array(rows) + first)
-                _check_sampled(w, li, Ls[li], rows, ref_idx, mem_d, kv_d, hid_in_rows, hidden_d,
+                _check_sampled(w, li, Ls[li], rows, ref_idx, ws, Tc, chunk, hid_in_rows, hidden_d,
                                gate_d, dead)
             del hidden_d
         E.engram_history_append(hist_c, tok_d, cu_d, tmap_d, pad)
@@ -222,10 +229,10 @@ def test_multimodal_batched_decode(E):
             rows = sorted(set([0, 1, 2, 127, 128, 255] + rng.integers(0, S, 4).tolist()))
             hid_in_rows = hidden_rows(cfg, cfg.layers[li], rows, batch=100 + step)
             gate_d = _forward(E, w, li, Ls[li], dtok_d, dcu_d, hist_all, tmap_d, hidden_d, ws, S)
-            idx_d, mem_d, kv_d = workspace_views(ws, S, cfg.H, cfg.hc)
+            idx_d = workspace_views(ws, S, cfg.H, cfg.hc)[0]
             ref_idx = O.hash_windows(win, dead, p.mult, p.prime, p.offset)
             assert np.array_equal(down32(idx_d).reshape(S, 24), ref_idx), (step, li)
-            _check_sampled(w, li, Ls[li], rows, ref_idx, mem_d, kv_d, hid_in_rows, hidden_d, gate_d, dead)
+            _check_sampled(w, li, Ls[li], rows, ref_idx, ws, S, S, hid_in_rows, hidden_d, gate_d, dead)
         E.engram_history_append(hist_all, dtok_d, dcu_d, tmap_d, pad)
         ref_hist = h_out
         assert np.array_equal(down32(hist_all).reshape(S, 3), ref_hist)

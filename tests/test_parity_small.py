@@ -12,7 +12,7 @@ import engram_synth as synth
 from oracle import engram_oracle as O
 from tests.conftest import gpu_available
 from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, down32, log,
-                               up8, up16, up32, upf, workspace_views)
+                               forward_rows, up8, up16, up32, upf, workspace_views)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
@@ -337,11 +337,11 @@ def _run_forward(E, w, li, tok, cu, hist, hidden, dot_scale=1.0):
                           gate_out=g_d, err_flags=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
-    nb = (T * 96 + 255) // 256 * 256
-    idx = down32(ws[: T * 96].view(torch.int32)).reshape(T, 24)
-    mem = down16(ws[nb: nb + T * 12288].view(torch.int16)).reshape(T, 6144)
-    nm = (T * 12288 + 255) // 256 * 256
-    kv = down16(ws[nb + nm: nb + nm + T * (cfg.hc + 1) * cfg.H * 2].view(torch.int16)).reshape(T, -1)
+    assert T <= 1024 and len(cu) - 1 <= 1024   # rows kept in position order
+    idx_d, _, mem_d, kv_d = workspace_views(ws, T, cfg.H, cfg.hc)
+    idx = down32(idx_d).reshape(T, 24)
+    mem = down16(mem_d).reshape(T, 6144)
+    kv = down16(kv_d).reshape(T, -1)
     return dict(idx=idx, mem=mem, kv=kv, hidden=down16(h_d).reshape(T, cfg.hc, cfg.H),
                 gate=g_d.cpu().numpy().reshape(T, cfg.hc)), (wkv, wqk)
 
@@ -437,7 +437,8 @@ def test_forward_small_batch_hash_gather_matches_stage_calls(E, S, T, n_bad):
     err_f = torch.zeros(1, dtype=torch.int32, device=DEV)
     ws = E.engram_forward(tok_d, cu_d, hist_d, tmap_d, p, codes, scales, wkv, wqk, hidden,
                           cfg.H, cfg.hc, err_flags=err_f)
-    idx_f, mem_f, _ = workspace_views(ws, T, cfg.H, cfg.hc)
+    idx_f = workspace_views(ws, T, cfg.H, cfg.hc)[0]
+    mem_f, _, has = forward_rows(ws, T, S, cfg.H, cfg.hc, np.arange(T))
     err_s = torch.zeros(1, dtype=torch.int32, device=DEV)
     idx_s = torch.empty(T * 24, dtype=torch.int32, device=DEV)
     mem_s = torch.empty(T * 6144, dtype=torch.int16, device=DEV)
@@ -446,9 +447,60 @@ def test_forward_small_batch_hash_gather_matches_stage_calls(E, S, T, n_bad):
     torch.cuda.synchronize()
     assert int(err_f.item()) == int(err_s.item()) == (1 if n_bad else 0)
     assert torch.equal(idx_f, idx_s)
-    assert torch.equal(mem_f, mem_s)
+    dead = tok == O.DEAD_TOKEN
+    assert np.all(has | dead)       # packed batches (above the limits) have no rows for DEAD positions
+    assert np.array_equal(mem_f[has], down16(mem_s).reshape(T, 6144)[has])
     if not n_bad:
         assert np.array_equal(down32(idx_f).reshape(T, 24), _ref_hash(tok, cu, hist, w.tmap, p))
+
+
+@pytest.mark.parametrize("H,hc", [(256, 4), (5120, 4), (5120, 2)])
+def test_forward_packs_live_rows_above_the_limits(E, H, hc):
+    """Above 1,024 tokens engram_forward decodes and projects only the live
+    (non-DEAD) positions, packed in order, and the gate reads each position's
+    k/v through that packing. Against the oracle on sampled rows (every DEAD
+    edge included) for each gate kernel (generic, streaming, per branch), plus
+    every DEAD row's hidden unchanged and its gate 0."""
+    log(f"forward: packed live rows, T=1,500 in 3 sequences with DEAD spans, H={H} hc={hc}")
+    w = World.of("tiny")
+    p = w.params[0]
+    rng = np.random.default_rng(H + hc)
+    lens = [700, 1, 799]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    tok = rng.integers(0, w.cfg.map_len, T).astype(np.uint32)
+    for a, n in ((100, 576), (690, 10), (701 + 5, 1), (701 + 50, 2)):   # image spans of 576, 10, 1, 2
+        tok[a:a + n] = O.DEAD_TOKEN
+    hist = rng.integers(0, w.cfg.vocab_c, (3, 3)).astype(np.uint32)
+    dead = tok == O.DEAD_TOKEN
+    wkv = synth.bf16_bits_from_f32(0.02 * rng.standard_normal(((hc + 1) * H, 6144)).astype(np.float32))
+    wqk = (1 + 0.1 * rng.standard_normal((hc, H))).astype(np.float32)
+    hidden = synth.bf16_bits_from_f32(rng.standard_normal((T, hc, H)).astype(np.float32))
+    codes, scales = device_table(E, p.n_rows, *w.keys[0])
+    h_d = up16(hidden)
+    g_d = torch.empty(T * hc, dtype=torch.float32, device=DEV)
+    ws = E.engram_forward(up32(tok), up32(cu), up32(hist), up32(w.tmap), p, codes, scales, up16(wkv),
+                          upf(wqk), h_d, H, hc, gate_out=g_d)
+    torch.cuda.synchronize()
+    ref_idx = _ref_hash(tok, cu, hist, w.tmap, p)
+    assert np.array_equal(down32(workspace_views(ws, T, H, hc)[0]).reshape(T, 24), ref_idx)
+    got_h = down16(h_d).reshape(T, hc, H)
+    got_g = g_d.cpu().numpy().reshape(T, hc)
+    assert np.array_equal(got_h[dead], hidden[dead]) and np.all(got_g[dead] == 0)
+    change = np.nonzero(np.diff(dead.astype(np.int8)))[0]
+    rows = np.unique(np.concatenate([change - 1, change, change + 1, change + 2, cu[:-1], cu[1:] - 1,
+                                     rng.integers(0, T, 40)]))
+    rows = rows[(rows >= 0) & (rows < T)]
+    got_mem, got_kv, has = forward_rows(ws, T, len(lens), H, hc, rows)
+    assert np.array_equal(has, ~dead[rows])
+    ref_mem = O.gather_decode(ref_idx[rows], w.rows(0))
+    assert np.array_equal(got_mem[has], ref_mem[has])
+    ref_kv = O.project(ref_mem, wkv)
+    assert_bf16_close(got_kv[has], ref_kv[has], what="kv")
+    new, g, dots = O.gate_residual(hidden[rows], ref_kv, wqk, dead[rows], H, hc, 1e-6, 1.0)
+    assert_bf16_close(got_h[rows].reshape(-1, H), new.reshape(-1, H), what="hidden")
+    well = np.abs(dots) >= 1e-2
+    assert np.max(np.abs(got_g[rows] - g)[well], initial=0.0) <= 1e-3
 
 
 def test_two_layers_on_a_side_stream_match_one_stream(E):
