@@ -186,7 +186,10 @@ int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const ui
 
 /* ---------------------------------------------------------------- whole layer */
 
-/* Workspace bytes engram_forward needs for T tokens (idx, mem and k/v). */
+/* Workspace bytes engram_forward needs for T tokens. Layout, each section
+ * 256-byte aligned: idx uint32[T][24] | slot uint32[T] | live count uint32
+ * and one uint32 per 4,096 positions | mem bf16[T][6144] | kv
+ * bf16[T][(hc+1)*H]. */
 size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
 
 /* One Engram layer: engram_hash -> engram_gather_decode -> engram_project ->
@@ -200,7 +203,13 @@ size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
  * For T <= 1024 tokens in S <= 1024 sequences (decode steps) hashing,
  * gathering and decoding run as one kernel, since both steps are chains of
  * dependent loads at that size; idx, mem and err_flags are bit-identical to
- * the two separate calls.
+ * the two separate calls, and mem/kv row t belongs to position t.
+ * Larger batches decode and project only the live (non-DEAD) positions: a
+ * DEAD position passes through the gate untouched, so its k/v are never
+ * read ([zLLM] 第四步: image rows skip the gate). slot[t] is then the mem/kv
+ * row of position t (rows packed in position order) or ENGRAM_DEAD_IDX, and
+ * the live count is read on the device (no host synchronisation). Hidden
+ * states and gates are the same either way.
  * stage_events: NULL, or ENGRAM_STAGE_EVENTS hipEvent_t created by the caller,
  * recorded before hashing, after hashing, after gather+decode, after the
  * projection and after the gate (with the single hash + gather kernel, the
