@@ -503,6 +503,55 @@ def test_forward_packs_live_rows_above_the_limits(E, H, hc):
     assert np.max(np.abs(got_g[rows] - g)[well], initial=0.0) <= 1e-3
 
 
+def test_decode_steps_replayed_from_a_graph_match_eager(E):
+    """Three decode steps (engram_forward, then the history append) captured in
+    a HIP graph and replayed three times, each replay from the same starting
+    history and hidden states restored by eager copies, give hidden states,
+    gates and history bit-identical to running the steps eagerly."""
+    log("forward: decode steps captured in a graph, three replays against eager")
+    w = World.of("tiny")
+    cfg, p = w.cfg, w.params[0]
+    S, steps = 16, 3
+    rng = np.random.default_rng(77)
+    cu = up32(np.arange(S + 1, dtype=np.int32))
+    toks = [up32(rng.integers(0, cfg.map_len, S).astype(np.uint32)) for _ in range(steps)]
+    hist0 = up32(rng.integers(0, cfg.vocab_c, (S, 3)).astype(np.uint32))
+    hidden0 = up16(synth.hidden_bf16(cfg, 1, S))
+    codes, scales = device_table(E, p.n_rows, *w.keys[0])
+    wkv = up16(synth.wkv_bf16(cfg, 1))
+    wqk = upf(synth.norm_weights(cfg, 1))
+    tmap = up32(w.tmap)
+    hist, hidden = hist0.clone(), hidden0.clone()
+    gates = [torch.empty(S * cfg.hc, dtype=torch.float32, device=DEV) for _ in range(steps)]
+    ws = torch.empty(E.engram_forward_workspace(S, cfg.H, cfg.hc), dtype=torch.uint8, device=DEV)
+
+    def run():
+        for i in range(steps):
+            E.engram_forward(toks[i], cu, hist, tmap, p, codes, scales, wkv, wqk, hidden, cfg.H, cfg.hc,
+                             ws=ws, gate_out=gates[i])
+            E.engram_history_append(hist, toks[i], cu, tmap, p.pad_cid)
+
+    run()
+    torch.cuda.synchronize()
+    ref = (hidden.clone(), hist.clone(), [g.clone() for g in gates])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        hist.copy_(hist0)
+        hidden.copy_(hidden0)
+        for g in gates:
+            g.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hidden, ref[0]), r
+        assert torch.equal(hist, ref[1]), r
+        for i in range(steps):
+            assert torch.equal(gates[i], ref[2][i]), (r, i)
+
+
 def test_two_layers_on_a_side_stream_match_one_stream(E):
     """Running one layer's engram_forward on a side stream beside another's
     (both read the same history; the append waits for both) gives the same
