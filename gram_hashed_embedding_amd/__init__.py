@@ -4,7 +4,7 @@ Argument marshalling only: every function checks the tensors' dtype, device
 and contiguity, then calls the C entry point of the same name with raw
 pointers and torch's current HIP stream. All computation happens in the HIP
 kernels; there is no CPU fallback. Importing this package fails if
-libengram.so has not been built (python -m gram_hashed_embedding_amd.build).
+libengram.so has not been built (python gram_hashed_embedding_amd/build.py).
 """
 from __future__ import annotations
 
@@ -74,7 +74,7 @@ class HashParams(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m gram_hashed_embedding_amd.build` (hipcc, gfx950)")
+                          "`python gram_hashed_embedding_amd/build.py` (hipcc, gfx950)")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, U32, U64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                       ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float,
@@ -89,11 +89,12 @@ def _load() -> ctypes.CDLL:
         "engram_history_append": ([P, P, P, I32, I64, P, U32, U32, P, P], ctypes.c_int),
         "engram_hash": ([P, P, I32, I64, P, P, U32, P, P, P, P], ctypes.c_int),
         "engram_gather_decode": ([P, I64, P, P, U64, P, P, P], ctypes.c_int),
-        "engram_project": ([P, I64, P, I32, I32, P, P], ctypes.c_int),
+        "engram_project": ([P, I64, P, P, I32, I32, P, P], ctypes.c_int),
+        "engram_pack_wkv": ([P, I32, I32, P, P], ctypes.c_int),
         "engram_gate": ([P, P, P, P, I64, I32, I32, F32, F32, P, P], ctypes.c_int),
         "engram_forward_workspace": ([I64, I32, I32], SZ),
-        "engram_forward": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, P, I32, I32, F32, F32,
-                            P, SZ, P, P, P, P], ctypes.c_int),
+        "engram_forward": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, P, P, I32, I32, F32,
+                            F32, P, SZ, P, P, P, P], ctypes.c_int),
         "engram_gen_table": ([P, P, U64, U64, U64, U64, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
@@ -246,16 +247,38 @@ def engram_gather_decode(idx, codes, scales, n_rows: int, mem, err_flags=None, s
         "engram_gather_decode")
 
 
-def engram_project(mem, wkv, H: int, hc: int, kv, stream=None) -> None:
+def _check_packed(wkv_packed, wkv) -> None:
+    if wkv_packed is not None and wkv_packed.numel() != wkv.numel():
+        raise ValueError("wkv_packed must have wkv's size (engram_pack_wkv's output)")
+
+
+def engram_project(mem, wkv, H: int, hc: int, kv, stream=None, wkv_packed=None) -> None:
     torch = _torch()
     T = mem.numel() // MEM
     if mem.numel() % MEM:
         raise ValueError("mem must hold T*6144 entries")
     if wkv.numel() != (hc + 1) * H * MEM or kv.numel() != T * (hc + 1) * H:
         raise ValueError("wkv must be [(hc+1)*H][6144] and kv [T][(hc+1)*H]")
+    _check_packed(wkv_packed, wkv)
     _check(lib.engram_project(_ptr(mem, _u16(torch), "mem"), T, _ptr(wkv, _u16(torch), "wkv"),
+                              _ptr(wkv_packed, _u16(torch), "wkv_packed", optional=True),
                               H, hc, _ptr(kv, _u16(torch), "kv"), _stream(stream)),
            "engram_project")
+
+
+def engram_pack_wkv(wkv, H: int, hc: int, out=None, stream=None):
+    """wkv in the decode layout (see include/engram.h); returns `out` (a new
+    tensor like wkv if None)."""
+    torch = _torch()
+    if wkv.numel() != (hc + 1) * H * MEM:
+        raise ValueError("wkv must be [(hc+1)*H][6144]")
+    if out is None:
+        out = torch.empty_like(wkv)
+    _check_packed(out, wkv)
+    _check(lib.engram_pack_wkv(_ptr(wkv, _u16(torch), "wkv"), H, hc,
+                               _ptr(out, _u16(torch), "wkv_packed"), _stream(stream)),
+           "engram_pack_wkv")
+    return out
 
 
 def engram_gate(hidden, kv, wqk, tok, H: int, hc: int, eps: float = 1e-6, dot_scale: float = 1.0,
@@ -282,7 +305,7 @@ def engram_forward_workspace(T: int, H: int, hc: int) -> int:
 def engram_forward(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv, wqk, hidden,
                    H: int, hc: int, eps: float = 1e-6, dot_scale: float = 1.0, ws=None,
                    gate_out=None, err_flags=None, stage_events: Optional[Sequence] = None,
-                   stream=None):
+                   stream=None, wkv_packed=None):
     """One Engram layer on the device. Returns the workspace tensor used
     (idx, mem and k/v live in it; pass it back in to reuse it)."""
     torch = _torch()
@@ -293,6 +316,7 @@ def engram_forward(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv,
         raise ValueError("hidden must be [T][hc][H]")
     if wkv.numel() != (hc + 1) * H * MEM or wqk.numel() != hc * H:
         raise ValueError("wkv must be [(hc+1)*H][6144] and wqk [hc][H]")
+    _check_packed(wkv_packed, wkv)
     _need(hist, 3 * S, "hist")
     _need(codes, p.n_rows * 256, "codes")
     _need(scales, p.n_rows * 8, "scales")
@@ -316,6 +340,7 @@ def engram_forward(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv,
         _ptr(hist, _u32(torch), "hist"), _ptr(token_map, _u32(torch), "token_map"),
         token_map.numel(), ctypes.byref(p), _ptr(codes, torch.uint8, "codes", host_ok=True),
         _ptr(scales, torch.uint8, "scales", host_ok=True), _ptr(wkv, _u16(torch), "wkv"),
+        _ptr(wkv_packed, _u16(torch), "wkv_packed", optional=True),
         _ptr(wqk, torch.float32, "wqk"), _ptr(hidden, _u16(torch), "hidden"), H, hc, eps,
         dot_scale, _ptr(ws, torch.uint8, "ws"), ws.numel(),
         _ptr(gate_out, torch.float32, "gate_out", optional=True),

@@ -1,6 +1,6 @@
 """Build libengram.so in-tree with hipcc for gfx950.
 
-    python -m gram_hashed_embedding_amd.build
+    python gram_hashed_embedding_amd/build.py
 
 Each source compiles to an object in _build/ (in parallel), then one
 `hipcc -shared` link writes gram_hashed_embedding_amd/libengram.so.

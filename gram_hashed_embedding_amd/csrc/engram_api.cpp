@@ -152,15 +152,15 @@ int check_gather_args(const uint32_t* idx, int64_t T, const uint8_t* codes, cons
 }
 
 // Host checks of engram_project's arguments (also applied by engram_forward).
-int check_project_args(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t H, int32_t hc,
-                       const uint16_t* kv) {
+int check_project_args(const uint16_t* mem, int64_t T, const uint16_t* wkv,
+                       const uint16_t* wkv_packed, int32_t H, int32_t hc, const uint16_t* kv) {
   int rc = check_dims(H, hc);
   if (rc != ENGRAM_OK) return rc;
   if (T < 0 || T > (int64_t)INT32_MAX) return fail(ENGRAM_EINVAL, "T out of range");
   if (T > 0) {
     if (!mem || !wkv || !kv) return fail(ENGRAM_EINVAL, "NULL pointer");
-    if (!aligned(mem, 16) || !aligned(wkv, 16) || !aligned(kv, 16))
-      return fail(ENGRAM_EINVAL, "mem, wkv and kv must be 16-byte aligned");
+    if (!aligned(mem, 16) || !aligned(wkv, 16) || !aligned(kv, 16) || !aligned(wkv_packed, 16))
+      return fail(ENGRAM_EINVAL, "mem, wkv, wkv_packed and kv must be 16-byte aligned");
   }
   return ENGRAM_OK;
 }
@@ -258,12 +258,25 @@ int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                   "engram_gather_decode");
 }
 
-int engram_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t H, int32_t hc,
-                   uint16_t* kv, hipStream_t stream) {
-  const int rc = check_project_args(mem, T, wkv, H, hc, kv);
+int engram_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, const uint16_t* wkv_packed,
+                   int32_t H, int32_t hc, uint16_t* kv, hipStream_t stream) {
+  const int rc = check_project_args(mem, T, wkv, wkv_packed, H, hc, kv);
   if (rc != ENGRAM_OK) return rc;
-  return from_hip(engram::launch_project(mem, T, nullptr, wkv, (hc + 1) * H, kv, stream),
+  return from_hip(engram::launch_project(mem, T, nullptr, wkv, wkv_packed, (hc + 1) * H, kv, stream),
                   "engram_project");
+}
+
+int engram_pack_wkv(const uint16_t* wkv, int32_t H, int32_t hc, uint16_t* wkv_packed,
+                    hipStream_t stream) {
+  const int rc = check_dims(H, hc);
+  if (rc != ENGRAM_OK) return rc;
+  if (!wkv || !wkv_packed) return fail(ENGRAM_EINVAL, "NULL pointer");
+  if (!aligned(wkv, 16) || !aligned(wkv_packed, 16))
+    return fail(ENGRAM_EINVAL, "wkv and wkv_packed must be 16-byte aligned");
+  const size_t bytes = (size_t)(hc + 1) * (size_t)H * ENGRAM_MEM * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(wkv), b = reinterpret_cast<uintptr_t>(wkv_packed);
+  if (a < b + bytes && b < a + bytes) return fail(ENGRAM_EINVAL, "wkv and wkv_packed overlap");
+  return from_hip(engram::launch_pack_wkv(wkv, (hc + 1) * H, wkv_packed, stream), "engram_pack_wkv");
 }
 
 int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const uint32_t* tok,
@@ -287,9 +300,10 @@ size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc) {
 int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
                    const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
                    const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,
-                   const uint16_t* wkv, const float* wqk, uint16_t* hidden, int32_t H, int32_t hc,
-                   float eps, float dot_scale, void* ws, size_t ws_bytes, float* gate_out,
-                   uint32_t* err_flags, hipEvent_t* stage_events, hipStream_t stream) {
+                   const uint16_t* wkv, const uint16_t* wkv_packed, const float* wqk,
+                   uint16_t* hidden, int32_t H, int32_t hc, float eps, float dot_scale, void* ws,
+                   size_t ws_bytes, float* gate_out, uint32_t* err_flags,
+                   hipEvent_t* stage_events, hipStream_t stream) {
   int rc = check_dims(H, hc);
   if (rc != ENGRAM_OK) return rc;
   const size_t need = engram_forward_workspace(T, H, hc);
@@ -313,7 +327,7 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
   // Every stage's arguments are checked before anything is enqueued.
   if ((rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx)) != ENGRAM_OK ||
       (rc = check_gather_args(idx, T, codes, scales, params->n_rows, mem)) != ENGRAM_OK ||
-      (rc = check_project_args(mem, T, wkv, H, hc, kv)) != ENGRAM_OK ||
+      (rc = check_project_args(mem, T, wkv, wkv_packed, H, hc, kv)) != ENGRAM_OK ||
       (rc = check_gate_args(hidden, kv, wqk, tok, T, H, hc, eps, gate_out)) != ENGRAM_OK)
     return rc;
   auto mark = [&](int i) -> int {
@@ -332,7 +346,7 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
     }
     if ((rc = mark(1)) != ENGRAM_OK) return rc;
     if ((rc = mark(2)) != ENGRAM_OK) return rc;
-    rc = from_hip(engram::launch_project(mem, T, nullptr, wkv, (hc + 1) * H, kv, stream),
+    rc = from_hip(engram::launch_project(mem, T, nullptr, wkv, wkv_packed, (hc + 1) * H, kv, stream),
                   "engram_forward: project");
     if (rc != ENGRAM_OK) return rc;
     if ((rc = mark(3)) != ENGRAM_OK) return rc;
@@ -359,7 +373,7 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
                 "engram_forward: gather + decode");
   if (rc != ENGRAM_OK) return rc;
   if ((rc = mark(2)) != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_project(mem, T, live, wkv, (hc + 1) * H, kv, stream),
+  rc = from_hip(engram::launch_project(mem, T, live, wkv, wkv_packed, (hc + 1) * H, kv, stream),
                 "engram_forward: project");
   if (rc != ENGRAM_OK) return rc;
   if ((rc = mark(3)) != ENGRAM_OK) return rc;

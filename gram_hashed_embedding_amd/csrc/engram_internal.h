@@ -47,8 +47,22 @@ hipError_t launch_hash_gather(const uint32_t* tok, const int32_t* cu, int32_t S,
                               hipStream_t st);
 // live_rows: NULL, or a device word holding how many of the T rows of mem
 // count (T > 256 only; rows past it are neither computed in full nor stored).
+// wkv_packed: NULL, or wkv in the packed decode layout (launch_pack_wkv),
+// which batches of at most kSkinnyMaxTokens tokens then read instead of wkv.
+constexpr int64_t kSkinnyMaxTokens = 256;
 hipError_t launch_project(const uint16_t* mem, int64_t T, const uint32_t* live_rows,
-                          const uint16_t* wkv, int32_t N, uint16_t* kv, hipStream_t st);
+                          const uint16_t* wkv, const uint16_t* wkv_packed, int32_t N, uint16_t* kv,
+                          hipStream_t st);
+// Packed decode layout of wkv[N][6144]: groups of pack_group_rows(N) rows
+// (256 groups, 16 to kPackMaxGroupRows rows each), cut in 16-row tiles whose
+// values are ordered [super-step of kPackSK][k-step][lane group][row][8].
+constexpr int kPackSK = 64;
+constexpr int kPackMaxGroupRows = 112;
+inline int pack_group_rows(int32_t N) {
+  const int g = (N + 255) / 256;
+  return g < 16 ? 16 : (g > kPackMaxGroupRows ? kPackMaxGroupRows : g);
+}
+hipError_t launch_pack_wkv(const uint16_t* wkv, int32_t N, uint16_t* out, hipStream_t st);
 // kv_row: NULL (position t reads kv row t), or the live_slots map.
 hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
                        const uint32_t* tok, const uint32_t* kv_row, int64_t T, int32_t H,

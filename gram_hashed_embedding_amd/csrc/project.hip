@@ -20,11 +20,13 @@
 //    each, loads staged through registers two K steps ahead and spread
 //    between the MFMAs.
 //  - skinny_kernel (T <= 256): the projection is a stream of wkv; the few mem
-//    rows sit in LDS and wkv rows go straight into registers.
+//    rows sit in LDS and wkv rows go straight into registers, read either
+//    from wkv itself or from its packed decode layout (pack_wkv_kernel).
 // Measured on the 25,600 x 6,144 wkv: the skinny kernel takes 78 / 95 / 104-117
-// us at T = 64 / 128 / 160-256, where the 256 x 256 kernel takes 128-147 us;
-// above T = 256 the 256 x 256 kernel wins (141-158 us at T = 384-512, where
-// 128 x 128 tiles took 233-255 us).
+// us at T = 64 / 128 / 160-256 on wkv and 51 / 65 / 86-110 us on the packed
+// layout, where the 256 x 256 kernel takes 128-147 us; above T = 256 the
+// 256 x 256 kernel wins (141-158 us at T = 384-512, where 128 x 128 tiles took
+// 233-255 us).
 
 #include "engram_internal.h"
 
@@ -336,9 +338,18 @@ typedef __attribute__((address_space(1))) const void* gptr_t;
 // super-step and a wave asks for 16 rows x 2*SK contiguous bytes at once. In
 // LDS, chunk c of mem row r sits in slot c ^ (r & 7), which keeps the 16-row
 // fragment reads free of bank conflicts.
+//
+// Read from wkv itself, each load instruction of a wave asks for 64 bytes of
+// each of 16 rows 12 KB apart, and the stream runs at about 4 TB/s. PK reads
+// the packed decode layout instead (pack_wkv_kernel), in which the 1 KB that
+// one load instruction of a wave takes is contiguous and a wave's whole tile
+// is one contiguous run, read with non-temporal loads (wkv is read once per
+// call): on its own that stream reaches 6.8 TB/s against 5.0 for the strided
+// one (no-compute probes, 315 MB, cold cache), and the kernel at T = 64 goes
+// from 78 to 51 us with bit-identical results (same fragments, same order).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int MT, int NC, int R, int U, int SK>
+template <int MT, int NC, int R, int U, int SK, bool PK>
 __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* __restrict__ A,
                                                                const uint16_t* __restrict__ B,
                                                                uint16_t* __restrict__ C, int M,
@@ -351,6 +362,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
   constexpr int STAGE = ROWS * ROWB;
   constexpr int INSTR = STAGE / 1024;        // 1 KB DMA instructions per stage
   static_assert(CH >= 8 && KS % U == 0 && KS > U, "super-step shape");
+  static_assert(!PK || SK == kPackSK, "the packed layout is cut in super-steps of kPackSK");
   static_assert(R >= 2 && R <= 4 && (R - 2) * INSTR <= 63, "ring depth vs vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[R * STAGE];
 
@@ -404,14 +416,38 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
   const int lim = (base + RW) < N ? (base + RW) : N;
   const int n0 = base + (wave - 1) * 16;
   const int arow = lane & 15, g = lane >> 4;
-  int nr = n0 + arow;
-  nr = nr < lim ? nr : lim - 1;
-  const uint16_t* bp = B + (int64_t)nr * K + g * J * 8;   // this lane's SK/4-value span
+  // B offsets of this lane's chunks: k-step j of super-step ks is at
+  // bp + ks * kstride + j * jstride.
+  const uint16_t* bp;
+  int jstride, kstride;
+  bool have_rows = true;
+  if constexpr (PK) {
+    // Tile of t_rows rows at n0, laid out [super-step][j][g][row][8 values]
+    // (pack_wkv_kernel); a wave whose tile lies past the group (small N)
+    // loads nothing, computes on zeros and stores nothing.
+    have_rows = n0 < lim;
+    const int t_rows = !have_rows ? 1 : (lim - n0 < 16 ? lim - n0 : 16);
+    const int prow = arow < t_rows ? arow : t_rows - 1;
+    bp = have_rows ? B + (int64_t)n0 * K + (g * t_rows + prow) * 8 : B;
+    jstride = 4 * t_rows * 8;
+    kstride = J * jstride;
+  } else {
+    int nr = n0 + arow;
+    nr = nr < lim ? nr : lim - 1;
+    bp = B + (int64_t)nr * K + g * J * 8;   // this lane's SK/4-value span
+    jstride = 8;
+    kstride = SK;
+  }
+  auto load_b = [&](int ks, int j) -> bf16x8 {
+    const bf16x8* q = reinterpret_cast<const bf16x8*>(bp + ks * kstride + j * jstride);
+    if constexpr (PK) return __builtin_nontemporal_load(q);
+    else return *q;
+  };
   bf16x8 bq[U][J];
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int j = 0; j < J; ++j) bq[u][j] = *reinterpret_cast<const bf16x8*>(bp + u * SK + j * 8);
+    for (int j = 0; j < J; ++j) bq[u][j] = have_rows ? load_b(u, j) : bf16x8{};
   f32x4 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -434,9 +470,10 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
     for (int u = 0; u < U; ++u) {
       const int ks = ks0 + u;
       step(ks, bq[u]);
+      if (have_rows) {
 #pragma unroll
-      for (int j = 0; j < J; ++j)
-        bq[u][j] = *reinterpret_cast<const bf16x8*>(bp + (ks + U) * SK + j * 8);
+        for (int j = 0; j < J; ++j) bq[u][j] = load_b(ks + U, j);
+      }
     }
   }
 #pragma unroll
@@ -457,17 +494,25 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
 
 // One workgroup per CU, each with an equal share of wkv rows (100 of 25,600
 // on 256 CUs): workgroups of a fixed 16*NC rows left CUs idle or doubly
-// loaded (25,600 rows are 6.25 tiles of 16 per CU), which cost 8-22%.
-template <int MT, int NC, int R, int U, int SK>
+// loaded (25,600 rows are 6.25 tiles of 16 per CU), which cost 8-22%. The
+// packed layout fixes its groups (pack_group_rows: 256 groups, one per CU of
+// an MI355X), so on it the workgroups are its groups.
+template <int MT, int NC, int R, int U, int SK, bool PK>
 hipError_t run_skinny(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t N, uint16_t* kv,
                       hipStream_t st) {
-  int n_cu = 0;
-  hipError_t e = cu_count(&n_cu);
-  if (e != hipSuccess) return e;
-  int rw = (N + n_cu - 1) / n_cu;
-  rw = rw < 16 ? 16 : (rw > 16 * NC ? 16 * NC : rw);
+  static_assert(16 * NC == kPackMaxGroupRows, "a workgroup holds the largest packed group");
+  int rw = 0;
+  if constexpr (PK) {
+    rw = pack_group_rows(N);
+  } else {
+    int n_cu = 0;
+    hipError_t e = cu_count(&n_cu);
+    if (e != hipSuccess) return e;
+    rw = (N + n_cu - 1) / n_cu;
+    rw = rw < 16 ? 16 : (rw > 16 * NC ? 16 * NC : rw);
+  }
   const int blocks = (N + rw - 1) / rw;
-  skinny_kernel<MT, NC, R, U, SK><<<blocks, 64 * (NC + 1), 0, st>>>(mem, wkv, kv, (int)T, N, rw);
+  skinny_kernel<MT, NC, R, U, SK, PK><<<blocks, 64 * (NC + 1), 0, st>>>(mem, wkv, kv, (int)T, N, rw);
   return hipGetLastError();
 }
 
@@ -483,16 +528,62 @@ hipError_t run_wave_tile(const uint16_t* mem, int64_t T, const uint32_t* live_ro
 }  // namespace
 
 hipError_t launch_project(const uint16_t* mem, int64_t T, const uint32_t* live_rows,
-                          const uint16_t* wkv, int32_t N, uint16_t* kv, hipStream_t st) {
+                          const uint16_t* wkv, const uint16_t* wkv_packed, int32_t N, uint16_t* kv,
+                          hipStream_t st) {
   if (T == 0) return hipSuccess;
   // <MT, NC, R, U, SK> chosen by sweeps on the 25,600 x 6,144 wkv stream
-  if (T <= 16) return run_skinny<1, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 32) return run_skinny<2, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 64) return run_skinny<4, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 128) return run_skinny<8, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 192) return run_skinny<12, 7, 4, 8, 64>(mem, T, wkv, N, kv, st);
-  if (T <= 256) return run_skinny<16, 7, 3, 8, 64>(mem, T, wkv, N, kv, st);
+  // (interleaved runs, 4 rotating copies of wkv so that none is cached).
+  if (T <= kSkinnyMaxTokens && wkv_packed != nullptr) {
+    const uint16_t* P = wkv_packed;
+    if (T <= 16) return run_skinny<1, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
+    if (T <= 32) return run_skinny<2, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
+    if (T <= 64) return run_skinny<4, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
+    if (T <= 128) return run_skinny<8, 7, 4, 2, 64, true>(mem, T, P, N, kv, st);
+    if (T <= 192) return run_skinny<12, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
+    return run_skinny<16, 7, 3, 3, 64, true>(mem, T, P, N, kv, st);
+  }
+  if (T <= 16) return run_skinny<1, 7, 4, 8, 64, false>(mem, T, wkv, N, kv, st);
+  if (T <= 32) return run_skinny<2, 7, 4, 8, 64, false>(mem, T, wkv, N, kv, st);
+  if (T <= 64) return run_skinny<4, 7, 4, 8, 64, false>(mem, T, wkv, N, kv, st);
+  if (T <= 128) return run_skinny<8, 7, 4, 8, 64, false>(mem, T, wkv, N, kv, st);
+  if (T <= 192) return run_skinny<12, 7, 4, 8, 64, false>(mem, T, wkv, N, kv, st);
+  if (T <= kSkinnyMaxTokens) return run_skinny<16, 7, 3, 8, 64, false>(mem, T, wkv, N, kv, st);
   return run_wave_tile(mem, T, live_rows, wkv, N, kv, st);
+}
+
+// ---------------------------------------------------------------- packed decode layout
+// One thread per 16-byte chunk (8 values) of wkv: chunk q of row n holds
+// k = 8q .. 8q+7, which is super-step s = q / 8, lane group g = (q % 8) / 2 and
+// k-step j = q % 2 of the skinny kernel's K order. Row n sits in group
+// n / G (G = pack_group_rows(N)), in that group's 16-row tile starting at
+// n0, which has t_rows rows (16, or fewer for a group's last tile); the chunk
+// goes to value offset n0 * 6144 + (((s * 2 + j) * 4 + g) * t_rows + i) * 8 of
+// the packed buffer, i = n - n0. Reads are coalesced, writes are 16-byte
+// pieces of 1 KB runs; it runs once per weight load.
+__global__ __launch_bounds__(256) void pack_wkv_kernel(const uint16_t* __restrict__ wkv,
+                                                       uint16_t* __restrict__ out, int N, int G) {
+  constexpr int QR = K / 8;   // chunks per row
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (int64_t)N * QR) return;
+  const int n = (int)(c / QR), q = (int)(c - (int64_t)n * QR);
+  const int grp = n / G, lr = n - grp * G;
+  const int glim = (N - grp * G) < G ? (N - grp * G) : G;   // rows in this group
+  const int t0 = lr & ~15, i = lr & 15;
+  const int t_rows = (glim - t0) < 16 ? (glim - t0) : 16;
+  const int s = q >> 3, g = (q & 7) >> 1, j = q & 1;
+  const int64_t n0 = (int64_t)grp * G + t0;
+  const int64_t dst = n0 * K + (int64_t)((((s * 2 + j) * 4 + g) * t_rows + i) * 8);
+  const uint4 v = *reinterpret_cast<const uint4*>(wkv + c * 8);
+  *reinterpret_cast<uint4*>(out + dst) = v;
+}
+
+hipError_t launch_pack_wkv(const uint16_t* wkv, int32_t N, uint16_t* out, hipStream_t st) {
+  static_assert(kPackSK == 64, "pack_wkv_kernel cuts K in super-steps of 64 values");
+  if (N <= 0) return hipSuccess;
+  const int64_t chunks = (int64_t)N * (K / 8);
+  const unsigned blocks = (unsigned)((chunks + 255) / 256);
+  pack_wkv_kernel<<<blocks, 256, 0, st>>>(wkv, out, N, pack_group_rows(N));
+  return hipGetLastError();
 }
 
 }  // namespace engram

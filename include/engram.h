@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 1
+#define ENGRAM_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 #define ENGRAM_OK            0
@@ -164,9 +164,31 @@ int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
  * ([zLLM] 第二步: wkv 25,600 x 6,144 BF16; [Storage] 旋转合同: the last 5,120
  * rows are V; [vLLM] How it works: one key per hyper-connection branch and
  * one shared value). Requires H % 64 == 0, 1 <= hc <= 8, 16-byte aligned
- * pointers. T may be 0. */
-int engram_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, int32_t H, int32_t hc,
-                   uint16_t* kv, hipStream_t stream);
+ * pointers. T may be 0.
+ * wkv_packed: NULL, or the same weights in the decode layout written by
+ * engram_pack_wkv (caller-owned, read-only here). Batches of at most 256
+ * tokens then stream wkv_packed instead of wkv; the results are
+ * bit-identical. Larger batches always read wkv. */
+int engram_project(const uint16_t* mem, int64_t T, const uint16_t* wkv, const uint16_t* wkv_packed,
+                   int32_t H, int32_t hc, uint16_t* kv, hipStream_t stream);
+
+/* Writes wkv[(hc+1)*H][6144] in the decode layout into wkv_packed (caller-
+ * owned device memory of the same size, 16-byte aligned, not overlapping
+ * wkv); once per weight load, enqueued on `stream`. A decode step reads all
+ * of wkv for a few tokens ([zLLM] AVX-512 BF16: decode gets no reuse of a
+ * weight load; the pages' CPU kernels read wkv in a packed block layout of
+ * their own), so it is bound by how fast wkv streams: in this layout each
+ * load instruction of the decode kernel reads 1 KB that is contiguous,
+ * where rows of wkv give it 64-byte pieces of 16 rows 12 KB apart.
+ * Layout, with N = (hc+1)*H and G = min(112, max(16, ceil(N / 256))): rows
+ * form groups of G (the last may be shorter), each cut in tiles of 16 rows
+ * (the group's last tile may be shorter, r rows in all). Value k of row n0+i
+ * of a tile starting at row n0, with k = 64s + 16g + 8j + e (s < 96, g < 4,
+ * j < 2, e < 8), sits at index n0*6144 + (((2s + j)*4 + g)*r + i)*8 + e.
+ * Returns ENGRAM_EINVAL for bad H/hc, NULL, misaligned or overlapping
+ * buffers. */
+int engram_pack_wkv(const uint16_t* wkv, int32_t H, int32_t hc, uint16_t* wkv_packed,
+                    hipStream_t stream);
 
 /* Context gate + residual, in place on hidden[T][hc][H] BF16.
  * For each non-DEAD token and branch b (DEAD = tok[t] == ENGRAM_DEAD_TOKEN,
@@ -200,6 +222,8 @@ size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
  * ENGRAM_EINVAL return leaves the stream untouched).
  * Per step: call once per layer with that layer's params/table/wkv/wqk and
  * hidden, all reading the same `hist`, then engram_history_append once.
+ * wkv_packed (NULL or engram_pack_wkv's output for this wkv) is passed on to
+ * the projection, which reads it for batches of at most 256 tokens.
  * For T <= 1024 tokens in S <= 1024 sequences (decode steps) hashing,
  * gathering and decoding run as one kernel, since both steps are chains of
  * dependent loads at that size; idx, mem and err_flags are bit-identical to
@@ -217,9 +241,10 @@ size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
 int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
                    const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
                    const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,
-                   const uint16_t* wkv, const float* wqk, uint16_t* hidden, int32_t H, int32_t hc,
-                   float eps, float dot_scale, void* ws, size_t ws_bytes, float* gate_out,
-                   uint32_t* err_flags, hipEvent_t* stage_events, hipStream_t stream);
+                   const uint16_t* wkv, const uint16_t* wkv_packed, const float* wqk,
+                   uint16_t* hidden, int32_t H, int32_t hc, float eps, float dot_scale, void* ws,
+                   size_t ws_bytes, float* gate_out, uint32_t* err_flags,
+                   hipEvent_t* stage_events, hipStream_t stream);
 
 /* ---------------------------------------------------------------- synthetic tables */
 

@@ -30,7 +30,8 @@ def test_header_declares_the_stage_entry_points():
     names = _declared()
     for n in ("engram_hash", "engram_gather_decode", "engram_project", "engram_gate",
               "engram_forward", "engram_history_append", "engram_history_fork",
-              "engram_history_reset", "engram_check_params", "engram_forward_workspace"):
+              "engram_history_reset", "engram_check_params", "engram_forward_workspace",
+              "engram_pack_wkv"):
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(E):
     assert not missing, missing
     for n in _declared():
         assert hasattr(E.lib, n)
-    assert E.lib.engram_abi_version() == 1
+    assert E.lib.engram_abi_version() == 2
 
 
 def test_status_strings(E):
@@ -108,26 +109,29 @@ def test_stage_entry_points_reject_bad_shapes_before_launch(E):
     hp = E.HashParams.from_any(p)
     fake = ctypes.c_void_p(0x10000)
     # H not a multiple of 64
-    assert L.engram_project(fake, 4, fake, 100, 4, fake, None) == -1
+    assert L.engram_project(fake, 4, fake, None, 100, 4, fake, None) == -1
     assert b"multiple of 64" in L.engram_last_error()
     # hc out of range
     assert L.engram_gate(fake, fake, fake, None, 4, 256, 9, 1e-6, 1.0, None, None) == -1
     # misaligned operand
-    assert L.engram_project(ctypes.c_void_p(0x10002), 4, fake, 256, 4, fake, None) == -1
+    assert L.engram_project(ctypes.c_void_p(0x10002), 4, fake, None, 256, 4, fake, None) == -1
+    assert L.engram_project(fake, 4, fake, ctypes.c_void_p(0x20008), 256, 4, fake, None) == -1
+    assert b"wkv_packed" in L.engram_last_error()
     # tokens without sequences
     assert L.engram_hash(fake, fake, 0, 5, fake, fake, 10, ctypes.byref(hp), fake, None, None) == -1
     # workspace too small
     need = L.engram_forward_workspace(8, 256, 4)
     assert need > 0
     rc = L.engram_forward(fake, fake, 1, 8, fake, fake, 10, ctypes.byref(hp), fake, fake, fake,
-                          fake, fake, 256, 4, 1e-6, 1.0, fake, need - 1, None, None, None, None)
+                          None, fake, fake, 256, 4, 1e-6, 1.0, fake, need - 1, None, None, None,
+                          None)
     assert rc == -1 and b"workspace" in L.engram_last_error()
     # bad params struct is caught by engram_hash too
     hp.prime[0] = 4
     assert L.engram_hash(fake, fake, 1, 5, fake, fake, 10, ctypes.byref(hp), fake, None, None) == -1
     # empty calls are no-ops that succeed without a device
     assert L.engram_gather_decode(None, 0, None, None, 0, None, None, None) == 0
-    assert L.engram_project(None, 0, None, 256, 4, None, None) == 0
+    assert L.engram_project(None, 0, None, None, 256, 4, None, None) == 0
 
 
 def test_forward_checks_its_stage_arguments_on_both_paths(E):
@@ -143,8 +147,8 @@ def test_forward_checks_its_stage_arguments_on_both_paths(E):
         ws = ctypes.c_void_p(0x100000)   # 256-byte aligned, never dereferenced
         def fwd(hp, codes=fake, scales=fake, tmap_len=10):
             return L.engram_forward(fake, fake, S, T, fake, fake, tmap_len, ctypes.byref(hp), codes,
-                                    scales, fake, fake, fake, H, hc, 1e-6, 1.0, ws, need, None, None,
-                                    None, None)
+                                    scales, fake, None, fake, fake, H, hc, 1e-6, 1.0, ws, need, None,
+                                    None, None, None)
         bad = E.HashParams.from_any(p)
         bad.prime[0] = 4
         assert fwd(bad) == -1, (S, T)
@@ -155,7 +159,23 @@ def test_forward_checks_its_stage_arguments_on_both_paths(E):
     # no tokens: nothing to launch, succeeds without a device
     hp = E.HashParams.from_any(p)
     assert L.engram_forward(None, fake, 1, 0, None, None, 0, ctypes.byref(hp), None, None, None,
-                            None, None, H, hc, 1e-6, 1.0, None, 0, None, None, None, None) == 0
+                            None, None, None, H, hc, 1e-6, 1.0, None, 0, None, None, None,
+                            None) == 0
+
+
+def test_pack_wkv_rejects_bad_arguments_before_launch(E):
+    """engram_pack_wkv checks shapes, pointers, alignment and overlap on the
+    host; none of these calls reaches a device."""
+    L = E.lib
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x40000000)
+    assert L.engram_pack_wkv(a, 100, 4, b, None) == -1                   # H % 64
+    assert L.engram_pack_wkv(a, 256, 0, b, None) == -1                   # hc
+    assert L.engram_pack_wkv(None, 256, 4, b, None) == -1
+    assert L.engram_pack_wkv(a, 256, 4, None, None) == -1
+    assert L.engram_pack_wkv(a, 256, 4, ctypes.c_void_p(0x40000004), None) == -1
+    # 5 x 256 rows x 12,288 B = 15.7 MB: a destination 1 MB past wkv overlaps it
+    assert L.engram_pack_wkv(a, 256, 4, ctypes.c_void_p(0x100000 + (1 << 20)), None) == -1
+    assert b"overlap" in L.engram_last_error()
 
 
 def test_workspace_size_formula(E):

@@ -282,6 +282,72 @@ def test_project_full_width(E, T):
     assert_bf16_close(down16(kv).reshape(T, -1), O.project(mem, wkv), what="kv")
 
 
+# ---------------------------------------------------------------- packed decode layout
+def _packed_index(N):
+    """Index in the packed buffer of every value of wkv[N][6144], written out
+    from the layout that include/engram.h states for engram_pack_wkv."""
+    G = min(112, max(16, -(-N // 256)))
+    n = torch.arange(N, device=DEV, dtype=torch.int64)
+    grp = n // G
+    lr = n - grp * G
+    glim = torch.clamp(N - grp * G, max=G)
+    t0 = (lr // 16) * 16
+    i = lr - t0
+    r = torch.clamp(glim - t0, max=16)
+    n0 = grp * G + t0
+    k = torch.arange(6144, device=DEV, dtype=torch.int64)
+    s, g, j, e = k // 64, (k % 64) // 16, (k % 16) // 8, k % 8
+    inner = ((2 * s + j) * 4 + g)[None, :] * r[:, None] + i[:, None]
+    return n0[:, None] * 6144 + inner * 8 + e[None, :]
+
+
+@pytest.mark.parametrize("H,hc", [(64, 1), (256, 4), (64, 2), (5120, 1), (5120, 4), (5120, 8)])
+def test_pack_wkv_matches_the_stated_layout(E, H, hc):
+    """engram_pack_wkv is the stated permutation: groups of 16-112 rows (the
+    last one short for hc = 8: 46,080 rows = 411 x 112 + 48), 16-row tiles
+    with a short last tile per group, and every value moved exactly once."""
+    N = (hc + 1) * H
+    log(f"pack_wkv: N={N}")
+    gen = torch.Generator(device=DEV).manual_seed(N)
+    wkv = torch.randint(-32768, 32767, (N, 6144), dtype=torch.int16, device=DEV, generator=gen)
+    packed = E.engram_pack_wkv(wkv, H, hc)
+    idx = _packed_index(N).reshape(-1)
+    assert int(idx.min().item()) >= 0 and int(idx.max().item()) < N * 6144
+    seen = torch.zeros(N * 6144, dtype=torch.bool, device=DEV)
+    seen[idx] = True     # N * 6144 indices reaching every slot: a permutation
+    assert bool(seen.all().item()), "layout is not a permutation"
+    want = torch.empty(N * 6144, dtype=torch.int16, device=DEV)
+    want[idx] = wkv.reshape(-1)
+    assert torch.equal(packed.reshape(-1), want)
+
+
+@pytest.mark.parametrize("H,hc", [(5120, 4), (256, 4), (64, 2), (5120, 1), (5120, 8)])
+def test_project_packed_matches_unpacked_bit_for_bit(E, H, hc):
+    """Every decode configuration (T <= 16 .. 256) reads the packed layout with
+    the same fragments in the same order as wkv itself, so kv is
+    bit-identical; T = 257 uses the 256 x 256 tiles, which ignore it. Sampled
+    rows of each T are also checked against the oracle. Small N leaves waves
+    of a workgroup without rows (N = 192: one 16-row tile per group)."""
+    N = (hc + 1) * H
+    rng = np.random.default_rng(N)
+    wkv = synth.bf16_bits_from_f32(0.02 * rng.standard_normal((N, 6144)).astype(np.float32))
+    wkv_d = up16(wkv)
+    packed = E.engram_pack_wkv(wkv_d, H, hc)
+    for T in (1, 16, 17, 33, 64, 65, 128, 129, 192, 193, 256, 257):
+        log(f"project packed vs unpacked: N={N} T={T}")
+        mem = synth.bf16_bits_from_f32(rng.standard_normal((T, 6144)).astype(np.float32) * 0.1)
+        mem_d = up16(mem)
+        a = torch.full((T * N,), 0x7FC1, dtype=torch.int16, device=DEV)
+        b = torch.full((T * N,), 0x7FC1, dtype=torch.int16, device=DEV)
+        E.engram_project(mem_d, wkv_d, H, hc, a)
+        E.engram_project(mem_d, wkv_d, H, hc, b, wkv_packed=packed)
+        torch.cuda.synchronize()
+        assert not torch.isnan(b.view(torch.bfloat16)).any().item(), T
+        assert torch.equal(a, b), T
+        rows = np.unique(np.array([0, T // 2, T - 1]))
+        assert_bf16_close(down16(b).reshape(T, N)[rows], O.project(mem[rows], wkv), what="kv")
+
+
 # ---------------------------------------------------------------- gate
 @pytest.mark.parametrize("dot_scale", [1.0, 1 / 16.0])
 @pytest.mark.parametrize("H,hc", [(256, 4), (64, 1), (5120, 4), (128, 8)])
@@ -322,7 +388,7 @@ def test_gate_without_dead_mask_and_zero_value(E):
 
 
 # ---------------------------------------------------------------- whole layer
-def _run_forward(E, w, li, tok, cu, hist, hidden, dot_scale=1.0):
+def _run_forward(E, w, li, tok, cu, hist, hidden, dot_scale=1.0, packed=False):
     cfg, p = w.cfg, w.params[li]
     kd, ks = w.keys[li]
     codes, scales = device_table(E, p.n_rows, kd, ks)
@@ -332,9 +398,11 @@ def _run_forward(E, w, li, tok, cu, hist, hidden, dot_scale=1.0):
     h_d = up16(hidden)
     g_d = torch.empty(T * cfg.hc, dtype=torch.float32, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    wkv_d = up16(wkv)
+    wkv_p = E.engram_pack_wkv(wkv_d, cfg.H, cfg.hc) if packed else None
     ws = E.engram_forward(up32(tok), up32(cu), up32(hist), up32(w.tmap), p, codes, scales,
-                          up16(wkv), upf(wqk), h_d, cfg.H, cfg.hc, 1e-6, dot_scale,
-                          gate_out=g_d, err_flags=err)
+                          wkv_d, upf(wqk), h_d, cfg.H, cfg.hc, 1e-6, dot_scale,
+                          gate_out=g_d, err_flags=err, wkv_packed=wkv_p)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     assert T <= 1024 and len(cu) - 1 <= 1024   # rows kept in position order
@@ -400,6 +468,11 @@ def test_forward_decode_config(E):
     got, (wkv, wqk) = _run_forward(E, w, 0, tok, cu, hist, hidden)
     ref = O.forward(tok, cu, hist, w.tmap, p, w.rows(0), wkv, wqk, hidden, cfg.H, cfg.hc)
     _check_forward(got, ref, cfg.hc, cfg.H)
+    # the same step with wkv also passed in the packed decode layout
+    got_p, _ = _run_forward(E, w, 0, tok, cu, hist, hidden, packed=True)
+    _check_forward(got_p, ref, cfg.hc, cfg.H)
+    for k in got:
+        assert np.array_equal(got_p[k], got[k]), k
 
 
 def _random_cut_batch(rng, S, T, map_len, vocab_c, n_bad=0):
@@ -519,6 +592,7 @@ def test_decode_steps_replayed_from_a_graph_match_eager(E):
     hidden0 = up16(synth.hidden_bf16(cfg, 1, S))
     codes, scales = device_table(E, p.n_rows, *w.keys[0])
     wkv = up16(synth.wkv_bf16(cfg, 1))
+    wkv_p = E.engram_pack_wkv(wkv, cfg.H, cfg.hc)
     wqk = upf(synth.norm_weights(cfg, 1))
     tmap = up32(w.tmap)
     hist, hidden = hist0.clone(), hidden0.clone()
@@ -527,8 +601,9 @@ def test_decode_steps_replayed_from_a_graph_match_eager(E):
 
     def run():
         for i in range(steps):
+            # the middle step reads wkv itself, the others its packed layout
             E.engram_forward(toks[i], cu, hist, tmap, p, codes, scales, wkv, wqk, hidden, cfg.H, cfg.hc,
-                             ws=ws, gate_out=gates[i])
+                             ws=ws, gate_out=gates[i], wkv_packed=None if i == 1 else wkv_p)
             E.engram_history_append(hist, toks[i], cu, tmap, p.pad_cid)
 
     run()
