@@ -420,15 +420,17 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
   // bp + ks * kstride + j * jstride.
   const uint16_t* bp;
   int jstride, kstride;
-  bool have_rows = true;
   if constexpr (PK) {
     // Tile of t_rows rows at n0, laid out [super-step][j][g][row][8 values]
-    // (pack_wkv_kernel); a wave whose tile lies past the group (small N)
-    // loads nothing, computes on zeros and stores nothing.
-    have_rows = n0 < lim;
-    const int t_rows = !have_rows ? 1 : (lim - n0 < 16 ? lim - n0 : 16);
+    // (pack_wkv_kernel). A wave whose tile lies past the group (small N)
+    // reads the group's last tile again and stores nothing: the loads stay
+    // unconditional, so the compiler keeps the U super-steps of loads in
+    // flight (a branch around them made it drain them at every step).
+    const int lt = base + ((lim - base - 1) & ~15);   // the group's last tile
+    const int tn = n0 < lim ? n0 : lt;
+    const int t_rows = lim - tn < 16 ? lim - tn : 16;
     const int prow = arow < t_rows ? arow : t_rows - 1;
-    bp = have_rows ? B + (int64_t)n0 * K + (g * t_rows + prow) * 8 : B;
+    bp = B + (int64_t)tn * K + (g * t_rows + prow) * 8;
     jstride = 4 * t_rows * 8;
     kstride = J * jstride;
   } else {
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int j = 0; j < J; ++j) bq[u][j] = have_rows ? load_b(u, j) : bf16x8{};
+    for (int j = 0; j < J; ++j) bq[u][j] = load_b(u, j);
   f32x4 acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -470,10 +472,8 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
     for (int u = 0; u < U; ++u) {
       const int ks = ks0 + u;
       step(ks, bq[u]);
-      if (have_rows) {
 #pragma unroll
-        for (int j = 0; j < J; ++j) bq[u][j] = load_b(ks + U, j);
-      }
+      for (int j = 0; j < J; ++j) bq[u][j] = load_b(ks + U, j);
     }
   }
 #pragma unroll
