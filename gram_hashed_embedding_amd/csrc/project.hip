@@ -23,7 +23,7 @@
 //    rows sit in LDS and wkv rows go straight into registers, read either
 //    from wkv itself or from its packed decode layout (pack_wkv_kernel).
 // Measured on the 25,600 x 6,144 wkv: the skinny kernel takes 78 / 95 / 104-117
-// us at T = 64 / 128 / 160-256 on wkv and 51 / 65 / 86-110 us on the packed
+// us at T = 64 / 128 / 160-256 on wkv and 51 / 64 / 78-91 us on the packed
 // layout, where the 256 x 256 kernel takes 128-147 us; above T = 256 the
 // 256 x 256 kernel wins (141-158 us at T = 384-512, where 128 x 128 tiles took
 // 233-255 us).
@@ -336,8 +336,11 @@ typedef __attribute__((address_space(1))) const void* gptr_t;
 // the sums unchanged: for K-step j, lane group g (lane >> 4) supplies chunk
 // g*J + j (8 values). So each lane reads SK/4 contiguous bytes of its row per
 // super-step and a wave asks for 16 rows x 2*SK contiguous bytes at once. In
-// LDS, chunk c of mem row r sits in slot c ^ (r & 7), which keeps the 16-row
-// fragment reads free of bank conflicts.
+// LDS, chunk c of mem row r sits in slot c ^ wt_swz(r) (the wave-tile
+// kernel's swizzle): a 16-row fragment read then covers all sixteen 16-byte
+// bank groups of a 256-byte span, since rows r and r + 8 take different
+// slots. With slot c ^ (r & 7) those two rows shared banks, a 2-way conflict
+// on every read, which cost 18% at T = 256 and 11% at T = 128 (same results).
 //
 // Read from wkv itself, each load instruction of a wave asks for 64 bytes of
 // each of 16 rows 12 KB apart, and the stream runs at about 4 TB/s. PK reads
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
       const int q = i * 64 + lane, r = q / CH, sl = q % CH;
-      const int c = sl ^ (r & 7);
+      const int c = sl ^ wt_swz(r);
       const int rr = r < M ? r : M - 1;
       off[i] = (uint32_t)rr * (K * 2) + c * 16;
     }
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int r = i * 16 + arow;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * ROWB + (((g * J + j) ^ (r & 7)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * ROWB + (((g * J + j) ^ wt_swz(r)) << 4));
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i], 0, 0, 0);
       }
     }
