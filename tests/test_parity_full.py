@@ -44,7 +44,9 @@ def _layer_inputs(E, w, li):
     log(f"  layer {cfg.layers[li]}: {p.n_rows:,}-row table on device in {__import__('time').time() - t0:.1f} s")
     wkv = synth.wkv_bf16(cfg, cfg.layers[li])
     wqk = synth.norm_weights(cfg, cfg.layers[li])
-    return dict(codes=codes, scales=scales, wkv=wkv, wkv_d=up16(wkv), wqk=wqk, wqk_d=upf(wqk))
+    wkv_d = up16(wkv)
+    wkv_p = E.engram_pack_wkv(wkv_d, cfg.H, cfg.hc)     # decode layout, as the benchmark uses it
+    return dict(codes=codes, scales=scales, wkv=wkv, wkv_d=wkv_d, wkv_p=wkv_p, wqk=wqk, wqk_d=upf(wqk))
 
 
 def _check_sampled(w, li, L, rows, idx_all, ws, T, S, hid_in, hid_out, gate_d, dead):
@@ -72,12 +74,14 @@ def _check_sampled(w, li, L, rows, idx_all, ws, T, S, hid_in, hid_out, gate_d, d
 
 
 def _forward(E, w, li, L, tok_d, cu_d, hist_d, tmap_d, hidden_d, ws, T):
+    """engram_forward as the benchmark calls it: wkv plus its packed decode
+    layout (read by batches of at most 256 tokens, ignored above)."""
     cfg = w.cfg
     gate_d = torch.empty(T * cfg.hc, dtype=torch.float32, device=DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     E.engram_forward(tok_d, cu_d, hist_d, tmap_d, w.params[li], L["codes"], L["scales"],
                      L["wkv_d"], L["wqk_d"], hidden_d, cfg.H, cfg.hc, 1e-6, 1.0, ws=ws,
-                     gate_out=gate_d, err_flags=err)
+                     gate_out=gate_d, err_flags=err, wkv_packed=L["wkv_p"])
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     return gate_d
