@@ -301,11 +301,14 @@ def _packed_index(N):
     return n0[:, None] * 6144 + inner * 8 + e[None, :]
 
 
-@pytest.mark.parametrize("H,hc", [(64, 1), (256, 4), (64, 2), (5120, 1), (5120, 4), (5120, 8)])
+@pytest.mark.parametrize("H,hc", [(64, 1), (256, 4), (64, 2), (5120, 1), (5120, 4), (5120, 8),
+                                  (2624, 1), (2752, 1)])
 def test_pack_wkv_matches_the_stated_layout(E, H, hc):
     """engram_pack_wkv is the stated permutation: groups of 16-112 rows (the
     last one short for hc = 8: 46,080 rows = 411 x 112 + 48), 16-row tiles
-    with a short last tile per group, and every value moved exactly once."""
+    with a short last tile per group (5,248 rows: groups of 21 = 16 + 5, the
+    last of 19 = 16 + 3; 5,504 rows: groups of 22, the last of 4), and every
+    value moved exactly once."""
     N = (hc + 1) * H
     log(f"pack_wkv: N={N}")
     gen = torch.Generator(device=DEV).manual_seed(N)
@@ -321,7 +324,8 @@ def test_pack_wkv_matches_the_stated_layout(E, H, hc):
     assert torch.equal(packed.reshape(-1), want)
 
 
-@pytest.mark.parametrize("H,hc", [(5120, 4), (256, 4), (64, 2), (5120, 1), (5120, 8)])
+@pytest.mark.parametrize("H,hc", [(5120, 4), (256, 4), (64, 2), (5120, 1), (5120, 8), (2624, 1),
+                                  (2752, 1)])
 def test_project_packed_matches_unpacked_bit_for_bit(E, H, hc):
     """Every decode configuration (T <= 16 .. 256) reads the packed layout with
     the same fragments in the same order as wkv itself, so kv is
