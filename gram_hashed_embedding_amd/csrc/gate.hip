@@ -206,59 +206,95 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
   }
 }
 
-// Small-T variant for H = 8 * THREADS: one workgroup per (token, branch),
-// so a decode batch of 64 tokens fills 256 workgroups instead of 64. Each
-// branch's gate needs only that branch's hidden and key (and every branch
-// the shared value, read once per branch). Thread i owns chunk i, and the
-// sums are formed and reduced in the same order as in gate_stream_kernel,
-// so the two kernels give identical bits.
-template <int THREADS>
+// Small-T variant for H = 8 * CPT * THREADS: one workgroup per (token,
+// branch), so a decode batch of 64 tokens fills 256 workgroups instead of 64.
+// Each branch's gate needs only that branch's hidden and key (and every
+// branch the shared value, read once per branch). Thread i owns chunks i,
+// i + THREADS, ...; the sums are formed per chunk and reduced per wave in the
+// same order as in gate_stream_kernel (chunk c's wave sums land where the
+// 640-thread layout's waves c * WAVES + w put theirs), so the kernels give
+// identical bits. CPT = 2 (320 threads) is for grids of more than three
+// 640-thread workgroups per CU, which would run in two rounds: at T = 256,
+// hc = 4 it takes 10.2 us against 12.0 (1,024 workgroups); at T <= 128 the
+// 640-thread form is faster (5.3 against 5.5 us at T = 64, 6.7 against 7.6
+// at T = 128).
+template <int THREADS, int CPT>
 __global__ __launch_bounds__(THREADS) void gate_branch_kernel(
     uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
     const uint32_t* __restrict__ tok, const uint32_t* __restrict__ kv_row, int hc, float eps,
     float dot_scale, float* __restrict__ gate_out) {
   constexpr int WAVES = THREADS / 64;
-  constexpr int H = THREADS * 8;
+  constexpr int H = THREADS * 8 * CPT;
   const int64_t t = blockIdx.x / hc;
   const int b = blockIdx.x - (int)t * hc;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tok != nullptr && tok[t] == ENGRAM_DEAD_TOKEN) {
     if (gate_out != nullptr && tid == 0) gate_out[t * hc + b] = 0.0f;
     return;
   }
-  uint16_t* h_t = hidden + (t * hc + b) * (int64_t)H + tid * 8;
+  uint16_t* h_b = hidden + (t * hc + b) * (int64_t)H;
   const int64_t T = gridDim.x / hc;
   const int64_t kr = kv_row == nullptr ? t : (int64_t)min(kv_row[t], (uint32_t)(T - 1));
-  const uint16_t* kv_t = kv + kr * (int64_t)(hc + 1) * H + tid * 8;
-  const uint4 hq = nt_load(h_t);
-  const uint4 kq = nt_load(kv_t + b * H);
-  const uint4 vq = nt_load(kv_t + hc * H);
-  const float4 w0 = *reinterpret_cast<const float4*>(wqk + b * H + tid * 8);
-  const float4 w1 = *reinterpret_cast<const float4*>(wqk + b * H + tid * 8 + 4);
-  const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  float h[8], k[8];
-  unpack8(hq, h);
-  unpack8(kq, k);
-  float s[3] = {0.0f, 0.0f, 0.0f};
+  const uint16_t* kv_t = kv + kr * (int64_t)(hc + 1) * H;
+  uint4 hq[CPT], kq[CPT], vq[CPT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    s[0] = fmaf(h[i], h[i], s[0]);
-    s[1] = fmaf(k[i], k[i], s[1]);
-    s[2] = fmaf(h[i] * k[i], w[i], s[2]);
+  for (int c = 0; c < CPT; ++c) {
+    const int e = (tid + c * THREADS) * 8;
+    hq[c] = nt_load(h_b + e);
+    kq[c] = nt_load(kv_t + b * H + e);
+    vq[c] = nt_load(kv_t + hc * H + e);
   }
-  __shared__ float red[3 * WAVES];
+  __shared__ float red[3 * CPT * WAVES];
   __shared__ float g_sh[1];
-  reduce_gates<1, WAVES>(s, red, g_sh, H, eps, dot_scale, nullptr, 0);
-  const float g = g_sh[0];
-  if (gate_out != nullptr && tid == 0) gate_out[t * hc + b] = g;
-  float v[8];
-  unpack8(vq, v);
-  uint32_t o[4];
+  float h[CPT][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = f32_to_bf16_rne(fmaf(g, v[2 * i], h[2 * i])) |
-           (f32_to_bf16_rne(fmaf(g, v[2 * i + 1], h[2 * i + 1])) << 16);
-  nt_store(h_t, o[0], o[1], o[2], o[3]);
+  for (int c = 0; c < CPT; ++c) {
+    const int e = (tid + c * THREADS) * 8;
+    const float4 w0 = *reinterpret_cast<const float4*>(wqk + b * H + e);
+    const float4 w1 = *reinterpret_cast<const float4*>(wqk + b * H + e + 4);
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float k[8];
+    unpack8(hq[c], h[c]);
+    unpack8(kq[c], k);
+    float s[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[0] = fmaf(h[c][i], h[c][i], s[0]);
+      s[1] = fmaf(k[i], k[i], s[1]);
+      s[2] = fmaf(h[c][i] * k[i], w[i], s[2]);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const float v = wave_sum(s[q]);
+      if (lane == 0) red[q * CPT * WAVES + c * WAVES + wave] = v;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float a = 0.f, k2 = 0.f, d = 0.f;
+#pragma unroll
+    for (int w = 0; w < CPT * WAVES; ++w) {
+      a += red[0 * CPT * WAVES + w];
+      k2 += red[1 * CPT * WAVES + w];
+      d += red[2 * CPT * WAVES + w];
+    }
+    const float g = gate_of(a, k2, d, 1.0f / (float)H, eps, dot_scale);
+    g_sh[0] = g;
+    if (gate_out != nullptr) gate_out[t * hc + b] = g;
+  }
+  __syncthreads();
+  const float g = g_sh[0];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    float v[8];
+    unpack8(vq[c], v);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = f32_to_bf16_rne(fmaf(g, v[2 * i], h[c][2 * i])) |
+             (f32_to_bf16_rne(fmaf(g, v[2 * i + 1], h[c][2 * i + 1])) << 16);
+    nt_store(h_b + (tid + c * THREADS) * 8, o[0], o[1], o[2], o[3]);
+  }
 }
 
 // Generic variant (any H % 64 == 0, hc <= 8): 256 threads, strided chunks,
@@ -356,8 +392,13 @@ hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
     if (e != hipSuccess) return e;
     if ((hc != 4 || T * hc <= 4 * (int64_t)n_cu) && T * hc <= (int64_t)INT32_MAX) {
       // decode-sized batches (and other branch counts): a workgroup per (token, branch)
-      gate_branch_kernel<640><<<(unsigned)(T * hc), 640, 0, st>>>(hidden, kv, wqk, tok, kv_row, hc,
-                                                                  eps, dot_scale, gate_out);
+      const unsigned grid = (unsigned)(T * hc);
+      if (T * hc > 3 * (int64_t)n_cu)
+        gate_branch_kernel<320, 2><<<grid, 320, 0, st>>>(hidden, kv, wqk, tok, kv_row, hc, eps,
+                                                         dot_scale, gate_out);
+      else
+        gate_branch_kernel<640, 1><<<grid, 640, 0, st>>>(hidden, kv, wqk, tok, kv_row, hc, eps,
+                                                         dot_scale, gate_out);
       return hipGetLastError();
     }
     if (hc == 4) {

@@ -721,10 +721,12 @@ def test_host_resident_table_matches_device_table(E):
 
 def test_gate_small_and_large_batch_kernels_agree_bitwise(E):
     """Up to 4 x (CU count) / hc tokens the gate runs one workgroup per
-    (token, branch); above that, one persistent workgroup per CU. Both form
-    and reduce the sums in the same order: the first 256 tokens of a
-    257-token call (persistent kernel) equal a 256-token call (per-branch
-    kernel) bit for bit, hidden and gates."""
+    (token, branch) (640 threads with one chunk each up to 3 x (CU count)
+    workgroups, 320 threads with two chunks each above); above that, one
+    persistent workgroup per CU. All form and reduce the sums in the same
+    order: on 256 CUs, the first 192 tokens of a 257-token call (persistent
+    kernel), a 256-token call (two chunks per thread) and a 192-token call
+    (one chunk per thread) agree bit for bit, hidden and gates."""
     cfg = synth.CONFIGS["decode"]
     H, hc, T = cfg.H, cfg.hc, 257
     rng = np.random.default_rng(21)
@@ -734,12 +736,13 @@ def test_gate_small_and_large_batch_kernels_agree_bitwise(E):
     tok = rng.integers(0, 1000, T).astype(np.uint32)
     tok[[3, 100]] = 0xFFFFFFFF
     outs = []
-    for n in (T, 256):
+    for n in (T, 256, 192):
         h = up16(hidden[:n])
         g = torch.empty(n * hc, dtype=torch.float32, device=DEV)
         E.engram_gate(h, up16(kv[:n]), upf(wqk), up32(tok[:n]), H, hc, gate_out=g)
         torch.cuda.synchronize()
-        outs.append((down16(h).reshape(n, hc, H)[:256], g.cpu().numpy().reshape(n, hc)[:256]))
-    assert np.array_equal(outs[0][0], outs[1][0])
-    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+        outs.append((down16(h).reshape(n, hc, H)[:192], g.cpu().numpy().reshape(n, hc)[:192]))
+    for o in outs[1:]:
+        assert np.array_equal(outs[0][0], o[0])
+        assert np.array_equal(outs[0][1].view(np.uint32), o[1].view(np.uint32))
     assert np.array_equal(outs[1][0][3], hidden[3]) and np.all(outs[1][1][[3, 100]] == 0)
