@@ -350,7 +350,21 @@ typedef __attribute__((address_space(1))) const void* gptr_t;
 // call): on its own that stream reaches 6.8 TB/s against 5.0 for the strided
 // one (no-compute probes, 315 MB, cold cache), and the kernel at T = 64 goes
 // from 78 to 51 us with bit-identical results (same fragments, same order).
+//
+// On the packed layout a super-step may also span two packed super-steps (SK
+// = 128): rows of 256 bytes in LDS (slot c ^ (r & 15)), half the barriers,
+// and the same MFMAs in the same order, so the same bits; at T = 128 it takes
+// 60 us against 66 (it gains nothing at T = 64 or at 192-256).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// LDS slot swizzle of a mem row with CH 16-byte chunks per stage: the 16
+// rows of a fragment read land in 16 distinct 16-byte bank groups.
+template <int CH>
+__device__ __forceinline__ int sk_swz(int r) {
+  static_assert(CH == 8 || CH == 16, "rows of 128 or 256 bytes");
+  if constexpr (CH == 8) return wt_swz(r);
+  else return r & 15;
+}
 
 template <int MT, int NC, int R, int U, int SK, bool PK>
 __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* __restrict__ A,
@@ -365,7 +379,9 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
   constexpr int STAGE = ROWS * ROWB;
   constexpr int INSTR = STAGE / 1024;        // 1 KB DMA instructions per stage
   static_assert(CH >= 8 && KS % U == 0 && KS > U, "super-step shape");
-  static_assert(!PK || SK == kPackSK, "the packed layout is cut in super-steps of kPackSK");
+  static_assert(!PK || SK == kPackSK || SK == 2 * kPackSK,
+                "a super-step spans one or two packed super-steps");
+  constexpr int P = PK ? SK / kPackSK : 1;   // packed super-steps per super-step
   static_assert(R >= 2 && R <= 4 && (R - 2) * INSTR <= 63, "ring depth vs vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[R * STAGE];
 
@@ -378,7 +394,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
       const int q = i * 64 + lane, r = q / CH, sl = q % CH;
-      const int c = sl ^ wt_swz(r);
+      const int c = sl ^ sk_swz<CH>(r);
       const int rr = r < M ? r : M - 1;
       off[i] = (uint32_t)rr * (K * 2) + c * 16;
     }
@@ -420,7 +436,9 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
   const int n0 = base + (wave - 1) * 16;
   const int arow = lane & 15, g = lane >> 4;
   // B offsets of this lane's chunks: k-step j of super-step ks is at
-  // bp + ks * kstride + j * jstride.
+  // bp + ks * kstride + j * jstride (wkv's rows), or at bp + (P * ks + j / 2)
+  // * kstride + (j % 2) * jstride (packed layout: kstride spans one packed
+  // super-step).
   const uint16_t* bp;
   int jstride, kstride;
   if constexpr (PK) {
@@ -435,7 +453,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
     const int prow = arow < t_rows ? arow : t_rows - 1;
     bp = B + (int64_t)tn * K + (g * t_rows + prow) * 8;
     jstride = 4 * t_rows * 8;
-    kstride = J * jstride;
+    kstride = 2 * jstride;
   } else {
     int nr = n0 + arow;
     nr = nr < lim ? nr : lim - 1;
@@ -444,9 +462,16 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
     kstride = SK;
   }
   auto load_b = [&](int ks, int j) -> bf16x8 {
-    const bf16x8* q = reinterpret_cast<const bf16x8*>(bp + ks * kstride + j * jstride);
-    if constexpr (PK) return __builtin_nontemporal_load(q);
-    else return *q;
+    if constexpr (PK)
+      return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(
+          bp + (P * ks + (j >> 1)) * kstride + (j & 1) * jstride));
+    else return *reinterpret_cast<const bf16x8*>(bp + ks * kstride + j * jstride);
+  };
+  // LDS chunk of mem holding the K values of k-step j for lane group g: the
+  // same K order as the B fragments above.
+  auto chunk_of = [&](int j) -> int {
+    if constexpr (PK) return (j >> 1) * 8 + g * 2 + (j & 1);
+    else return g * J + j;
   };
   bf16x8 bq[U][J];
 #pragma unroll
@@ -464,7 +489,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void skinny_kernel(const uint16_t* _
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int r = i * 16 + arow;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * ROWB + (((g * J + j) ^ wt_swz(r)) << 4));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((chunk_of(j) ^ sk_swz<CH>(r)) << 4));
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i], 0, 0, 0);
       }
     }
@@ -541,7 +566,7 @@ hipError_t launch_project(const uint16_t* mem, int64_t T, const uint32_t* live_r
     if (T <= 16) return run_skinny<1, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
     if (T <= 32) return run_skinny<2, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
     if (T <= 64) return run_skinny<4, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
-    if (T <= 128) return run_skinny<8, 7, 4, 2, 64, true>(mem, T, P, N, kv, st);
+    if (T <= 128) return run_skinny<8, 7, 3, 2, 128, true>(mem, T, P, N, kv, st);
     if (T <= 192) return run_skinny<12, 7, 4, 4, 64, true>(mem, T, P, N, kv, st);
     return run_skinny<16, 7, 3, 3, 64, true>(mem, T, P, N, kv, st);
   }
