@@ -23,7 +23,7 @@
 //    rows sit in LDS and wkv rows go straight into registers, read either
 //    from wkv itself or from its packed decode layout (pack_wkv_kernel).
 // Measured on the 25,600 x 6,144 wkv: the skinny kernel takes 78 / 95 / 104-117
-// us at T = 64 / 128 / 160-256 on wkv and 51 / 64 / 78-91 us on the packed
+// us at T = 64 / 128 / 160-256 on wkv and 51 / 62 / 78-91 us on the packed
 // layout, where the 256 x 256 kernel takes 128-147 us; above T = 256 the
 // 256 x 256 kernel wins (141-158 us at T = 384-512, where 128 x 128 tiles took
 // 233-255 us).
