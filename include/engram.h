@@ -43,7 +43,7 @@ extern "C" {
 #define ENGRAM_OK            0
 #define ENGRAM_EINVAL       (-1)  /* host-side shape, pointer, alignment or parameter check failed */
 #define ENGRAM_EHIP         (-2)  /* a HIP launch or runtime call failed */
-#define ENGRAM_EUNSUPPORTED (-3)  /* valid request this build does not handle (e.g. not gfx950) */
+#define ENGRAM_EUNSUPPORTED (-3)  /* valid request this library does not handle (e.g. not gfx950) */
 
 /* Device-side error bits (ORed into *err_flags when err_flags != NULL). */
 #define ENGRAM_ERR_TOKEN_RANGE 0x1u  /* a non-DEAD token id >= map_len (hashed as pad_cid) */
