@@ -54,7 +54,8 @@ hipError_t launch_project(const uint16_t* mem, int64_t T, const uint32_t* live_r
                           const uint16_t* wkv, const uint16_t* wkv_packed, int32_t N, uint16_t* kv,
                           hipStream_t st);
 // Packed decode layout of wkv[N][6144]: groups of pack_group_rows(N) rows
-// (256 groups, 16 to kPackMaxGroupRows rows each), cut in 16-row tiles whose
+// (ceil(N / 256) kept within 16..kPackMaxGroupRows, so 256 groups unless the
+// clamp applies; the last group may be shorter), cut in 16-row tiles whose
 // values are ordered [super-step of kPackSK][k-step][lane group][row][8].
 constexpr int kPackSK = 64;
 constexpr int kPackMaxGroupRows = 112;
