@@ -284,8 +284,8 @@ int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const ui
                 hipStream_t stream) {
   const int rc = check_gate_args(hidden, kv, wqk, tok, T, H, hc, eps, gate_out);
   if (rc != ENGRAM_OK) return rc;
-  return from_hip(engram::launch_gate(hidden, kv, wqk, tok, nullptr, T, H, hc, eps, dot_scale, gate_out,
-                                      stream),
+  return from_hip(engram::launch_gate(hidden, kv, wqk, tok, nullptr, nullptr, nullptr, T, H, hc, eps,
+                                      dot_scale, gate_out, stream),
                   "engram_gate");
 }
 
@@ -294,7 +294,7 @@ size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc) {
   const size_t t = (size_t)T;
   return round256(t * ENGRAM_BUCKETS * 4) + round256(t * 4) +
          round256(4 * (1 + (size_t)engram::live_chunks(T))) + round256(t * ENGRAM_MEM * 2) +
-         round256(t * (size_t)(hc + 1) * (size_t)H * 2);
+         round256(t * (size_t)(hc + 1) * (size_t)H * 2) + round256(t * 4);
 }
 
 int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
@@ -313,13 +313,15 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
     if (!aligned(ws, 256)) return fail(ENGRAM_EINVAL, "workspace must be 256-byte aligned");
   }
   // Workspace: idx [T][24] | slot [T] | live count + per-chunk counts |
-  // mem | kv, each section 256-byte aligned.
+  // mem | kv | live positions [T], each section 256-byte aligned.
   uint8_t* w = static_cast<uint8_t*>(ws);
   const size_t t = T > 0 ? (size_t)T : 0;
   const size_t o_slot = round256(t * ENGRAM_BUCKETS * 4), o_count = o_slot + round256(t * 4);
   const size_t o_mem = o_count + round256(4 * (1 + (size_t)engram::live_chunks((int64_t)t)));
   const size_t o_kv = o_mem + round256(t * ENGRAM_MEM * 2);
+  const size_t o_pos = o_kv + round256(t * (size_t)(hc + 1) * (size_t)H * 2);
   uint32_t* idx = reinterpret_cast<uint32_t*>(w);
+  uint32_t* live_pos = reinterpret_cast<uint32_t*>(w + o_pos);
   uint32_t* slot = reinterpret_cast<uint32_t*>(w + o_slot);
   uint32_t* live = reinterpret_cast<uint32_t*>(w + o_count);
   uint16_t* mem = reinterpret_cast<uint16_t*>(w + o_mem);
@@ -350,8 +352,8 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
                   "engram_forward: project");
     if (rc != ENGRAM_OK) return rc;
     if ((rc = mark(3)) != ENGRAM_OK) return rc;
-    rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, nullptr, T, H, hc, eps, dot_scale,
-                                      gate_out, stream),
+    rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, nullptr, nullptr, nullptr, T, H, hc, eps,
+                                      dot_scale, gate_out, stream),
                   "engram_forward: gate");
     if (rc != ENGRAM_OK) return rc;
     return mark(4);
@@ -359,13 +361,15 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
   // Larger batches: only live (non-DEAD) positions are decoded and projected.
   // DEAD positions pass through the gate untouched, so their k/v are never
   // read; the live rows of mem and kv are packed in position order, slot[t]
-  // locating position t's, and the projection reads the live count on the
-  // device, so nothing waits on the host.
+  // locating position t's and live_pos[i] the position of row i, and the
+  // projection and the gate read the live count on the device, so nothing
+  // waits on the host.
   rc = from_hip(engram::launch_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, idx,
                                     err_flags, stream),
                 "engram_forward: hash");
   if (rc != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_live_slots(tok, T, slot, live, live + 1, stream), "engram_forward: live slots");
+  rc = from_hip(engram::launch_live_slots(tok, T, slot, live, live + 1, live_pos, stream),
+                "engram_forward: live slots");
   if (rc != ENGRAM_OK) return rc;
   if ((rc = mark(1)) != ENGRAM_OK) return rc;
   rc = from_hip(engram::launch_gather_decode(idx, T, codes, scales, params->n_rows, mem, slot,
@@ -377,8 +381,8 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
                 "engram_forward: project");
   if (rc != ENGRAM_OK) return rc;
   if ((rc = mark(3)) != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, slot, T, H, hc, eps, dot_scale, gate_out,
-                                    stream),
+  rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, slot, live_pos, live, T, H, hc, eps,
+                                    dot_scale, gate_out, stream),
                 "engram_forward: gate");
   if (rc != ENGRAM_OK) return rc;
   return mark(4);

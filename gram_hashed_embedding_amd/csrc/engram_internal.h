@@ -23,12 +23,13 @@ hipError_t launch_hash(const uint32_t* tok, const int32_t* cu, int32_t S, int64_
                        const engram_hash_params& p, uint32_t* idx, uint32_t* err,
                        hipStream_t st);
 // Rows of the live (non-DEAD) positions of tok[T]: slot[t] = live positions
-// before t (ENGRAM_DEAD_IDX for a DEAD one), *count = live positions.
-// chunk_count: scratch of live_chunks(T) words.
+// before t (ENGRAM_DEAD_IDX for a DEAD one), *count = live positions, and,
+// when live_pos is given, live_pos[slot[t]] = t (the live positions in
+// order). chunk_count: scratch of live_chunks(T) words.
 constexpr int64_t kLiveChunkPositions = 4096;
 inline int64_t live_chunks(int64_t T) { return (T + kLiveChunkPositions - 1) / kLiveChunkPositions; }
 hipError_t launch_live_slots(const uint32_t* tok, int64_t T, uint32_t* slot, uint32_t* count,
-                             uint32_t* chunk_count, hipStream_t st);
+                             uint32_t* chunk_count, uint32_t* live_pos, hipStream_t st);
 // slot: NULL (position t's rows go to mem row t), or the live_slots map
 // (they go to row slot[t]; DEAD positions write nothing).
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
@@ -64,10 +65,14 @@ inline int pack_group_rows(int32_t N) {
   return g < 16 ? 16 : (g > kPackMaxGroupRows ? kPackMaxGroupRows : g);
 }
 hipError_t launch_pack_wkv(const uint16_t* wkv, int32_t N, uint16_t* out, hipStream_t st);
-// kv_row: NULL (position t reads kv row t), or the live_slots map.
+// kv_row: NULL (position t reads kv row t), or the live_slots map. live_pos,
+// live_count: NULL, or launch_live_slots' live_pos and count for the same
+// tokens (kv_row given too): the kernels that walk tokens then walk the live
+// rows only.
 hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
-                       const uint32_t* tok, const uint32_t* kv_row, int64_t T, int32_t H,
-                       int32_t hc, float eps, float dot_scale, float* gate_out, hipStream_t st);
+                       const uint32_t* tok, const uint32_t* kv_row, const uint32_t* live_pos,
+                       const uint32_t* live_count, int64_t T, int32_t H, int32_t hc, float eps,
+                       float dot_scale, float* gate_out, hipStream_t st);
 hipError_t launch_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin,
                             uint64_t n_rows, uint64_t key_data, uint64_t key_scale,
                             hipStream_t st);

@@ -102,12 +102,20 @@ __device__ __forceinline__ void nt_store(uint16_t* p, uint32_t a, uint32_t b, ui
 // moves no HBM bytes; its sums are discarded and its hidden is not stored.
 //
 // kv_row, when given, maps a position to its row of kv (the projection then
-// ran over the live positions only); otherwise position t reads row t.
+// ran over the live positions only); otherwise position t reads row t. With
+// live_pos and live_count as well (the live positions in order and their
+// number), the workgroups walk the live rows i < *live_count instead, each
+// reading kv row i and hidden position live_pos[i]: DEAD positions cost no
+// time (walking them took as long as a live token, since every step waits
+// on the workgroup's reduction; the multimodal prefill, 56% DEAD, spent
+// 1.54 ms per 65,536-position chunk in the gate), and a last light pass
+// writes their zero gates.
 template <int HC, int THREADS>
 __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
     uint16_t* __restrict__ hidden, const uint16_t* __restrict__ kv, const float* __restrict__ wqk,
-    const uint32_t* __restrict__ tok, const uint32_t* __restrict__ kv_row, int64_t T, float eps,
-    float dot_scale, float* __restrict__ gate_out) {
+    const uint32_t* __restrict__ tok, const uint32_t* __restrict__ kv_row,
+    const uint32_t* __restrict__ live_pos, const uint32_t* __restrict__ live_count, int64_t T,
+    float eps, float dot_scale, float* __restrict__ gate_out) {
   constexpr int WAVES = THREADS / 64;
   constexpr int H = THREADS * 8;
   static_assert((HC + 1) * H * 2 <= HC * H * 4, "stand-in rows must fit in the norm weights");
@@ -129,17 +137,28 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
 #pragma unroll
     for (int b = 0; b < HC; ++b) hq[b] = nt_load(h_t + b * H);
   };
-  // Liveness and kv row of this workgroup's tokens, 64 at a time: lane i of
-  // `flags` and `rows` holds token blockIdx.x + (k0 + i) * G (0 past the end).
+  // The workgroup's walk is w = blockIdx.x + it * G, over positions, or over
+  // live rows (live mode). Liveness, kv row and hidden position of its steps,
+  // 64 at a time: lane i of `flags`, `rows` and `hpos` holds step k0 + i
+  // (0 past the end).
+  const bool live_mode = live_pos != nullptr && live_count != nullptr;
+  const int64_t n_walk = live_mode ? min((int64_t)*live_count, T) : T;
   const int lane = tid & 63;
-  uint32_t flags = 0, rows = 0;
+  uint32_t flags = 0, rows = 0, hpos = 0;
   auto load_meta = [&](int64_t k0) {
-    const int64_t tt = blockIdx.x + (k0 + lane) * G;
-    const bool in = tt < T;
-    flags = (in && (tok == nullptr || tok[tt] != ENGRAM_DEAD_TOKEN)) ? 1u : 0u;
-    // (clamped: a DEAD position's map entry is never used, and no entry may
-    // leave kv)
-    rows = kv_row == nullptr ? (uint32_t)tt : (in ? min(kv_row[tt], (uint32_t)(T - 1)) : 0u);
+    const int64_t w = blockIdx.x + (k0 + lane) * G;
+    const bool in = w < n_walk;
+    if (live_mode) {
+      flags = in ? 1u : 0u;
+      rows = in ? (uint32_t)w : 0u;
+      hpos = in ? min(live_pos[w], (uint32_t)(T - 1)) : 0u;
+    } else {
+      flags = (in && (tok == nullptr || tok[w] != ENGRAM_DEAD_TOKEN)) ? 1u : 0u;
+      // (clamped: a DEAD position's map entry is never used, and no entry
+      // may leave kv)
+      rows = kv_row == nullptr ? (uint32_t)w : (in ? min(kv_row[w], (uint32_t)(T - 1)) : 0u);
+      hpos = (uint32_t)w;
+    }
   };
   load_meta(0);
   auto live_at = [&](int64_t it) -> bool {
@@ -148,18 +167,22 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
   auto row_at = [&](int64_t it) -> int64_t {
     return (int64_t)(uint32_t)__builtin_amdgcn_readlane(rows, (int)(it & 63));
   };
+  auto pos_at = [&](int64_t it) -> int64_t {
+    return (int64_t)(uint32_t)__builtin_amdgcn_readlane(hpos, (int)(it & 63));
+  };
 
-  int64_t it = 0, t = blockIdx.x;
+  int64_t it = 0;
   bool lv = live_at(0);
   bool lvn = live_at(1);
   int64_t kr = row_at(0), krn = row_at(1);
+  int64_t t = pos_at(0), tn = pos_at(1);
   load_hv(t, kr, lv);
   load_k(kr, lv);
-  for (; t < T; t += G, ++it) {
-    const int64_t tn = t + G;
+  for (int64_t w = blockIdx.x; w < n_walk; w += G, ++it) {
     if (((it + 2) & 63) == 0) load_meta(it + 2);
     const bool lvnn = live_at(it + 2);
     const int64_t krnn = row_at(it + 2);
+    const int64_t tnn = pos_at(it + 2);
     float s[3 * HC];
 #pragma unroll
     for (int b = 0; b < HC; ++b) {
@@ -195,14 +218,24 @@ __global__ __launch_bounds__(THREADS) void gate_stream_kernel(
                  (f32_to_bf16_rne(fmaf(g, v[2 * i + 1], h[2 * i + 1])) << 16);
         nt_store(h_t + b * H, o[0], o[1], o[2], o[3]);
       }
-    } else if (gate_out != nullptr && tid < HC) {
+    } else if (gate_out != nullptr && tid < HC && w < T) {
       gate_out[t * HC + tid] = 0.0f;
     }
     load_hv(tn, krn, lvn);
     lv = lvn;
     lvn = lvnn;
     krn = krnn;
+    t = tn;
+    tn = tnn;
     __syncthreads();   // keeps the waves of the workgroup on the same token
+  }
+  if (live_mode && gate_out != nullptr && tok != nullptr) {
+    // the DEAD positions, which the walk skipped: gate 0
+    for (int64_t q = (int64_t)blockIdx.x * THREADS + tid; q < T; q += G * THREADS)
+      if (tok[q] == ENGRAM_DEAD_TOKEN) {
+#pragma unroll
+        for (int b = 0; b < HC; ++b) gate_out[q * HC + b] = 0.0f;
+      }
   }
 }
 
@@ -383,8 +416,9 @@ __global__ __launch_bounds__(kGenThreads) void gate_generic_kernel(
 }  // namespace
 
 hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
-                       const uint32_t* tok, const uint32_t* kv_row, int64_t T, int32_t H,
-                       int32_t hc, float eps, float dot_scale, float* gate_out, hipStream_t st) {
+                       const uint32_t* tok, const uint32_t* kv_row, const uint32_t* live_pos,
+                       const uint32_t* live_count, int64_t T, int32_t H, int32_t hc, float eps,
+                       float dot_scale, float* gate_out, hipStream_t st) {
   if (T == 0) return hipSuccess;
   if (H == 5120) {
     int n_cu = 0;
@@ -405,8 +439,8 @@ hipError_t launch_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk,
       // one resident workgroup per CU (the kernel keeps two tokens' loads in
       // registers, so a second workgroup would not fit beside it)
       const unsigned grid = (unsigned)(T < n_cu ? T : n_cu);
-      gate_stream_kernel<4, 640><<<grid, 640, 0, st>>>(hidden, kv, wqk, tok, kv_row, T, eps,
-                                                       dot_scale, gate_out);
+      gate_stream_kernel<4, 640><<<grid, 640, 0, st>>>(hidden, kv, wqk, tok, kv_row, live_pos,
+                                                       live_count, T, eps, dot_scale, gate_out);
       return hipGetLastError();
     }
   }

@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kLiveThreads) void live_slots_kernel(const uint32_t
                                                                   int64_t T,
                                                                   const uint32_t* __restrict__ chunk_count,
                                                                   uint32_t* __restrict__ slot,
-                                                                  uint32_t* __restrict__ count) {
+                                                                  uint32_t* __restrict__ count,
+                                                                  uint32_t* __restrict__ live_pos) {
   constexpr int WAVES = kLiveThreads / 64;
   __shared__ uint32_t sh[WAVES], wave_tot[WAVES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -135,8 +136,15 @@ __global__ __launch_bounds__(kLiveThreads) void live_slots_kernel(const uint32_t
   }
   uint32_t r = before + incl - c;
 #pragma unroll
-  for (int i = 0; i < kLivePer; ++i)
-    if (t0 + i < T) slot[t0 + i] = ((live >> i) & 1u) ? r++ : ENGRAM_DEAD_IDX;
+  for (int i = 0; i < kLivePer; ++i) {
+    if (t0 + i >= T) continue;
+    if ((live >> i) & 1u) {
+      if (live_pos != nullptr) live_pos[r] = (uint32_t)(t0 + i);   // the inverse map
+      slot[t0 + i] = r++;
+    } else {
+      slot[t0 + i] = ENGRAM_DEAD_IDX;
+    }
+  }
   if (blockIdx.x == gridDim.x - 1 && tid == WAVES * 64 - 1) *count = r;   // the last live row + 1
   (void)chunk_total;
 }
@@ -169,11 +177,11 @@ hipError_t launch_history_append(uint32_t* hist, const uint32_t* tok, const int3
 }
 
 hipError_t launch_live_slots(const uint32_t* tok, int64_t T, uint32_t* slot, uint32_t* count,
-                             uint32_t* chunk_count, hipStream_t st) {
+                             uint32_t* chunk_count, uint32_t* live_pos, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const unsigned chunks = (unsigned)((T + kLiveChunk - 1) / kLiveChunk);
   live_count_kernel<<<chunks, kLiveThreads, 0, st>>>(tok, T, chunk_count);
-  live_slots_kernel<<<chunks, kLiveThreads, 0, st>>>(tok, T, chunk_count, slot, count);
+  live_slots_kernel<<<chunks, kLiveThreads, 0, st>>>(tok, T, chunk_count, slot, count, live_pos);
   return hipGetLastError();
 }
 

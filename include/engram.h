@@ -211,7 +211,8 @@ int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const ui
 /* Workspace bytes engram_forward needs for T tokens. Layout, each section
  * 256-byte aligned: idx uint32[T][24] | slot uint32[T] | live count uint32
  * and one uint32 per 4,096 positions | mem bf16[T][6144] | kv
- * bf16[T][(hc+1)*H]. */
+ * bf16[T][(hc+1)*H] | live positions uint32[T] (position of each packed
+ * row, for batches above the small-batch limits). */
 size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
 
 /* One Engram layer: engram_hash -> engram_gather_decode -> engram_project ->

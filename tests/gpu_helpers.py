@@ -125,8 +125,8 @@ def hidden_rows(cfg, layer: int, rows, batch: int = 0) -> np.ndarray:
 
 def workspace_views(ws: torch.Tensor, T: int, H: int, hc: int):
     """Device views (idx [T][24], slot [T], mem [T][6144], kv [T][(hc+1)H]) of
-    engram_forward's workspace: idx | slot | live counts | mem | kv,
-    each section 256-byte aligned. Batches of more than 1,024 tokens or
+    engram_forward's workspace: idx | slot | live counts | mem | kv | live
+    positions, each section 256-byte aligned. Batches of more than 1,024 tokens or
     sequences pack the live (non-DEAD) positions' mem and kv rows in position
     order (row slot[t] for position t); smaller ones keep row t for position t."""
     r = lambda x: (x + 255) // 256 * 256
@@ -138,6 +138,14 @@ def workspace_views(ws: torch.Tensor, T: int, H: int, hc: int):
     mem = ws[o_mem: o_mem + T * 12288].view(torch.int16)
     kv = ws[o_kv: o_kv + T * (hc + 1) * H * 2].view(torch.int16)
     return idx, slot, mem, kv
+
+
+def live_positions(ws: torch.Tensor, T: int, H: int, hc: int):
+    """Device view of the workspace's last section: the position of each packed
+    (live) row, in row order, for batches that pack rows."""
+    r = lambda x: (x + 255) // 256 * 256
+    o_pos = r(T * 96) + r(T * 4) + r(4 * (1 + (T + 4095) // 4096)) + r(T * 12288) + r(T * (hc + 1) * H * 2)
+    return ws[o_pos: o_pos + T * 4].view(torch.int32)
 
 
 def forward_rows(ws: torch.Tensor, T: int, S: int, H: int, hc: int, rows):

@@ -181,10 +181,10 @@ def test_pack_wkv_rejects_bad_arguments_before_launch(E):
 def test_workspace_size_formula(E):
     T, H, hc = 1000, 5120, 4
     r = lambda x: (x + 255) // 256 * 256
-    # idx | slot | live count and one count per 4,096 positions | mem | kv
+    # idx | slot | live count and one count per 4,096 positions | mem | kv | live positions
     for T in (1, 1000, 4096, 4097, 50032):
         assert E.engram_forward_workspace(T, H, hc) == (r(T * 96) + r(T * 4) + r(4 * (1 + (T + 4095) // 4096))
-                                                        + r(T * 12288) + r(T * 25600 * 2))
+                                                        + r(T * 12288) + r(T * 25600 * 2) + r(T * 4))
     assert E.engram_forward_workspace(0, H, hc) == 0
 
 

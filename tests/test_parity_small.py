@@ -12,7 +12,7 @@ import engram_synth as synth
 from oracle import engram_oracle as O
 from tests.conftest import gpu_available
 from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, down32, log,
-                               forward_rows, up8, up16, up32, upf, workspace_views)
+                               forward_rows, up8, up16, up32, upf, workspace_views, live_positions)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
@@ -555,15 +555,24 @@ def test_forward_packs_live_rows_above_the_limits(E, H, hc):
     hidden = synth.bf16_bits_from_f32(rng.standard_normal((T, hc, H)).astype(np.float32))
     codes, scales = device_table(E, p.n_rows, *w.keys[0])
     h_d = up16(hidden)
-    g_d = torch.empty(T * hc, dtype=torch.float32, device=DEV)
+    g_d = torch.full((T * hc,), float("nan"), dtype=torch.float32, device=DEV)
     ws = E.engram_forward(up32(tok), up32(cu), up32(hist), up32(w.tmap), p, codes, scales, up16(wkv),
                           upf(wqk), h_d, H, hc, gate_out=g_d)
     torch.cuda.synchronize()
     ref_idx = _ref_hash(tok, cu, hist, w.tmap, p)
     assert np.array_equal(down32(workspace_views(ws, T, H, hc)[0]).reshape(T, 24), ref_idx)
+    # slot and the live positions are inverse maps over the live positions
+    slot = down32(workspace_views(ws, T, H, hc)[1])
+    n_live = int((~dead).sum())
+    pos = down32(live_positions(ws, T, H, hc))[:n_live]
+    assert np.array_equal(pos, np.nonzero(~dead)[0]) and np.array_equal(slot[pos], np.arange(n_live))
     got_h = down16(h_d).reshape(T, hc, H)
     got_g = g_d.cpu().numpy().reshape(T, hc)
     assert np.array_equal(got_h[dead], hidden[dead]) and np.all(got_g[dead] == 0)
+    # every live position was gated (not only the sampled ones below)
+    lg = got_g[~dead]
+    assert np.all(np.isfinite(lg) & (lg >= 0) & (lg <= 1))      # written: the buffer held NaN
+    assert np.all((got_h != hidden).any(axis=(1, 2))[~dead])
     change = np.nonzero(np.diff(dead.astype(np.int8)))[0]
     rows = np.unique(np.concatenate([change - 1, change, change + 1, change + 2, cu[:-1], cu[1:] - 1,
                                      rng.integers(0, T, 40)]))
