@@ -150,6 +150,28 @@ def make_hash_params(root: int, layer: int, vocab_c: int, prime_base: int,
                       pad_cid=pad_cid)
 
 
+def make_full_range_hash_params(root: int, layer: int, vocab_c: int, prime_base: int,
+                                pad_cid: int) -> HashParams:
+    """Like make_hash_params, but with 96 distinct odd multipliers drawn
+    uniformly over [2^32, 2^64), one per (bucket, window slot): products of a
+    compressed id and a multiplier wrap past 2^64 and XORs of them reach
+    2^63 and above, so every bucket's own multipliers and the 64-bit wrap
+    are exercised (the C ABI takes any uint64 table)."""
+    base = make_hash_params(root, layer, vocab_c, prime_base, pad_cid)
+    rng = np.random.default_rng([root, STREAM_MULT, layer, 1])
+    seen = set()
+    mult = np.zeros((N_BUCKETS, 4), dtype=np.uint64)
+    for j in range(N_BUCKETS):
+        for k in range(4):
+            while True:
+                m = int(rng.integers(1 << 31, 1 << 63, dtype=np.uint64)) * 2 + 1
+                if m not in seen:
+                    seen.add(m)
+                    mult[j, k] = m
+                    break
+    return dataclasses.replace(base, mult=mult)
+
+
 # --------------------------------------------------------------------------
 # Token map: seeded many-to-one map raw id -> compressed id, onto 0..V_c-1
 # (stand-in for the tokenizer normalisation of [vLLM] "How it works").

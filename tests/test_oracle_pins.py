@@ -318,6 +318,29 @@ def test_hash_special_cases():
     assert O.hash_windows(w, np.ones(1, bool), mult, prime, offset)[0].tolist() == [O.DEAD_IDX] * 24
 
 
+def test_hash_full_range_multipliers_match_big_integer_arithmetic():
+    """With 96 distinct full-range multipliers (products wrap past 2^64, XORs
+    reach 2^63 and above, each bucket has its own), the vectorised uint64
+    hash equals exact arithmetic on Python integers reduced mod 2^64 by hand:
+    per bucket j of order n, x = XOR over k < n of (w_k * m[j][k] mod 2^64),
+    row = offset[j] + x mod prime[j]."""
+    p = synth.make_full_range_hash_params(0xE46A0002, 1, 100_000, 666_666, 0)
+    rng = np.random.default_rng(9)
+    wins = rng.integers(0, 100_000, (300, 4)).astype(np.uint64)
+    got = O.hash_windows(wins, np.zeros(len(wins), bool), p.mult, p.prime, p.offset)
+    wrapped = high = 0
+    for w, row in zip(wins.tolist(), got.tolist()):
+        for j in range(24):
+            x = 0
+            for k in range(2 + j // 8):
+                prod = int(w[k]) * int(p.mult[j][k])
+                wrapped += prod >= 1 << 64
+                x ^= prod % (1 << 64)
+            high += x >= 1 << 63
+            assert row[j] == int(p.offset[j]) + x % int(p.prime[j])
+    assert wrapped > 1000 and high > 1000       # the inputs do exercise the wrap and the top bit
+
+
 # ---------------------------------------------------------------- decode
 def _fixture_bytes():
     with open(os.path.join(GOLDEN, "e4m3_bytes.txt")) as f:
@@ -497,6 +520,48 @@ def test_gate_scale_invariance_and_sign():
     wsw = wqk[[1, 0, 2, 3]]
     d1 = O.gate_dots(hsw, ksw, wsw, H, hc, 1e-30, 1.0)
     assert np.allclose(d1[:, [1, 0, 2, 3]], d0, rtol=1e-12)
+
+
+def test_gate_dot_per_branch_weight_constants():
+    """wqk[b] = c_b everywhere, h_b = k_b, s = 1: dot_b = c_b * H * m_b / (m_b + eps)
+    with m_b = mean(h_b^2). Distinct c_b per branch, so a dropped weight or a
+    weight taken from another branch changes every dot ([zLLM] 第三步: each
+    branch carries its own premultiplied q/k weights)."""
+    H, hc, eps = 256, 4, 1e-6
+    hidden, kv, _ = _gate_inputs(H=H, seed=5)
+    kv[:, : hc * H] = hidden.reshape(hidden.shape[0], -1)
+    c = np.array([0.5, 1.25, 2.0, 3.0], np.float32)
+    wqk = np.repeat(c[:, None], H, axis=1).astype(np.float32)
+    dots = O.gate_dots(hidden, kv, wqk, H, hc, eps, 1.0)
+    h = O.bf16_to_f64(hidden)
+    m = np.mean(h * h, axis=2)
+    assert np.allclose(dots, c[None, :] * H * m / (m + eps), rtol=1e-12)
+
+
+def test_gate_dot_one_hot_weight_selects_one_product():
+    """Hidden entries +-a and key entries +-k (so RMS a and k exactly, eps -> 0)
+    and a one-hot wqk[b] = w_b at column i_b: dot_b = s * sign(h_i k_i) * w_b,
+    whatever a and k. Each branch has its own column and weight, so the
+    weights of the wrong branch, or no weights, give other values."""
+    H, hc, T = 128, 4, 3
+    rng = np.random.default_rng(11)
+    a, kmag = 0.5, 2.0                                        # exact in BF16
+    hs = rng.choice([-1.0, 1.0], (T, hc, H))
+    ks = rng.choice([-1.0, 1.0], (T, hc, H))
+    hidden = O.bf16_rne(a * hs)
+    kv = np.zeros((T, (hc + 1) * H), np.uint16)
+    kv[:, : hc * H] = O.bf16_rne(kmag * ks).reshape(T, hc * H)
+    cols = [3, 70, 101, 127]
+    w = [0.75, -1.5, 2.5, 4.0]
+    wqk = np.zeros((hc, H), np.float32)
+    for b in range(hc):
+        wqk[b, cols[b]] = w[b]
+    for s in (1.0, 1 / 16):
+        dots = O.gate_dots(hidden, kv, wqk, H, hc, 0.0, s)
+        for t in range(T):
+            for b in range(hc):
+                want = s * hs[t, b, cols[b]] * ks[t, b, cols[b]] * w[b]
+                assert dots[t, b] == pytest.approx(want, rel=1e-12), (t, b)
 
 
 def test_residual_closed_form_and_pass_through():
