@@ -18,8 +18,9 @@ __all__ = [
     "EngramError", "HashParams", "lib",
     "engram_check_params", "engram_history_reset", "engram_history_fork",
     "engram_history_append", "engram_hash", "engram_gather_decode", "engram_project",
-    "engram_gate", "engram_forward_workspace", "engram_forward", "engram_gen_table",
-    "DEAD_TOKEN", "DEAD_IDX", "BUCKETS", "MEM", "STAGE_EVENTS",
+    "engram_gate", "engram_forward_workspace", "engram_precompute", "engram_gate_precomputed",
+    "engram_forward", "engram_gen_table", "engram_pack_wkv",
+    "DEAD_TOKEN", "DEAD_IDX", "BUCKETS", "MEM", "STAGE_EVENTS", "PRECOMPUTE_STAGE_ROWS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ DEAD_IDX = 0xFFFFFFFF
 BUCKETS = 24
 MEM = 6144
 STAGE_EVENTS = 5
+PRECOMPUTE_STAGE_ROWS = 0x1
 
 ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EHIP, ENGRAM_EUNSUPPORTED = 0, -1, -2, -3
 
@@ -93,6 +95,10 @@ def _load() -> ctypes.CDLL:
         "engram_pack_wkv": ([P, I32, I32, P, P], ctypes.c_int),
         "engram_gate": ([P, P, P, P, I64, I32, I32, F32, F32, P, P], ctypes.c_int),
         "engram_forward_workspace": ([I64, I32, I32], SZ),
+        "engram_precompute": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, I32, I32, U32, P, SZ,
+                               P, P], ctypes.c_int),
+        "engram_gate_precomputed": ([P, P, SZ, P, I32, I64, P, I32, I32, F32, F32, P, P],
+                                    ctypes.c_int),
         "engram_forward": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, P, P, I32, I32, F32,
                             F32, P, SZ, P, P, P, P], ctypes.c_int),
         "engram_gen_table": ([P, P, U64, U64, U64, U64, P], ctypes.c_int),
@@ -300,6 +306,56 @@ def engram_gate(hidden, kv, wqk, tok, H: int, hc: int, eps: float = 1e-6, dot_sc
 
 def engram_forward_workspace(T: int, H: int, hc: int) -> int:
     return int(lib.engram_forward_workspace(T, H, hc))
+
+
+def engram_precompute(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv, H: int,
+                      hc: int, ws=None, flags: int = 0, err_flags=None, stream=None,
+                      wkv_packed=None):
+    """The hidden-independent half of one layer (hash, gather + decode,
+    projection) into a workspace. Returns the workspace (allocated here when
+    None; pass the same one to engram_gate_precomputed)."""
+    torch = _torch()
+    p = HashParams.from_any(params)
+    S = cu_seqlens.numel() - 1
+    T = tok.numel()
+    if wkv.numel() != (hc + 1) * H * MEM:
+        raise ValueError("wkv must be [(hc+1)*H][6144]")
+    _check_packed(wkv_packed, wkv)
+    _need(hist, 3 * S, "hist")
+    _need(codes, p.n_rows * 256, "codes")
+    _need(scales, p.n_rows * 8, "scales")
+    _need(err_flags, 1, "err_flags")
+    need = engram_forward_workspace(T, H, hc)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=wkv.device)
+    _need(ws, need, "ws")
+    _check(lib.engram_precompute(
+        _ptr(tok, _u32(torch), "tok"), _ptr(cu_seqlens, _i32(torch), "cu_seqlens"), S, T,
+        _ptr(hist, _u32(torch), "hist"), _ptr(token_map, _u32(torch), "token_map"),
+        token_map.numel(), ctypes.byref(p), _ptr(codes, torch.uint8, "codes", host_ok=True),
+        _ptr(scales, torch.uint8, "scales", host_ok=True), _ptr(wkv, _u16(torch), "wkv"),
+        _ptr(wkv_packed, _u16(torch), "wkv_packed", optional=True), H, hc, flags,
+        _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _ptr(err_flags, _u32(torch), "err_flags", optional=True), _stream(stream)),
+        "engram_precompute")
+    return ws
+
+
+def engram_gate_precomputed(hidden, ws, tok, S: int, wqk, H: int, hc: int, eps: float = 1e-6,
+                            dot_scale: float = 1.0, gate_out=None, stream=None) -> None:
+    """The gate at layer entry, reading the k/v engram_precompute left in ws
+    for the same tokens (S sequences)."""
+    torch = _torch()
+    T = tok.numel()
+    if hidden.numel() != T * hc * H or wqk.numel() != hc * H:
+        raise ValueError("hidden must be [T][hc][H] and wqk [hc][H]")
+    _need(gate_out, T * hc, "gate_out")
+    _need(ws, engram_forward_workspace(T, H, hc), "ws")
+    _check(lib.engram_gate_precomputed(
+        _ptr(hidden, _u16(torch), "hidden"), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _ptr(tok, _u32(torch), "tok"), S, T, _ptr(wqk, torch.float32, "wqk"), H, hc, eps,
+        dot_scale, _ptr(gate_out, torch.float32, "gate_out", optional=True), _stream(stream)),
+        "engram_gate_precomputed")
 
 
 def engram_forward(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv, wqk, hidden,

@@ -119,8 +119,6 @@ int check_dims(int32_t H, int32_t hc) {
   return ENGRAM_OK;
 }
 
-size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
-
 // Host checks of engram_hash's arguments (also applied by engram_forward).
 int check_hash_args(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
                     const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
@@ -181,7 +179,158 @@ int check_gate_args(const uint16_t* hidden, const uint16_t* kv, const float* wqk
   return ENGRAM_OK;
 }
 
+// Host checks of engram_precompute's arguments (also applied by engram_forward).
+int check_precompute_args(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                          const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                          const engram_hash_params* params, const uint8_t* codes,
+                          const uint8_t* scales, const uint16_t* wkv, const uint16_t* wkv_packed,
+                          int32_t H, int32_t hc, uint32_t flags, void* ws, size_t ws_bytes) {
+  int rc = check_dims(H, hc);
+  if (rc != ENGRAM_OK) return rc;
+  if (flags & ~(uint32_t)ENGRAM_PRECOMPUTE_STAGE_ROWS)
+    return fail(ENGRAM_EINVAL, "unknown precompute flags 0x%x", flags);
+  if (T > 0) {
+    const size_t need = engram_forward_workspace(T, H, hc);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(ENGRAM_EINVAL, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (!aligned(ws, 256)) return fail(ENGRAM_EINVAL, "workspace must be 256-byte aligned");
+  }
+  const engram::WorkspaceLayout w = engram::workspace_layout(ws, T > 0 ? T : 0, H, hc);
+  if ((rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, w.idx)) != ENGRAM_OK ||
+      (rc = check_gather_args(w.idx, T, codes, scales, params->n_rows, w.mem)) != ENGRAM_OK ||
+      (rc = check_project_args(w.mem, T, wkv, wkv_packed, H, hc, w.kv)) != ENGRAM_OK)
+    return rc;
+  return ENGRAM_OK;
+}
+
+// Enqueues hash -> gather + decode -> projection into the workspace.
+// ev: NULL, or 4 events recorded before hashing, after hashing, after
+// gather + decode and after the projection.
+int enqueue_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                       const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                       const engram_hash_params& params, const uint8_t* codes, const uint8_t* scales,
+                       const uint16_t* wkv, const uint16_t* wkv_packed, int32_t H, int32_t hc,
+                       uint32_t flags, void* ws, uint32_t* err_flags, hipEvent_t* ev,
+                       hipStream_t stream) {
+  int rc;
+  auto mark = [&](int i) -> int {
+    if (ev == nullptr) return ENGRAM_OK;
+    return from_hip(hipEventRecord(ev[i], stream), "engram_precompute: hipEventRecord");
+  };
+  if ((rc = mark(0)) != ENGRAM_OK) return rc;
+  const engram::WorkspaceLayout w = engram::workspace_layout(ws, T, H, hc);
+  const bool stage = (flags & ENGRAM_PRECOMPUTE_STAGE_ROWS) != 0;
+  const bool packed = engram::packs_rows(T, S);
+  const uint32_t* slot = packed ? w.slot : nullptr;
+  if (T > 0 && !packed && !stage) {
+    // Small batch: one kernel hashes, gathers and decodes; events 1 and 2
+    // both mark its end.
+    rc = from_hip(engram::launch_hash_gather(tok, cu_seqlens, S, T, hist, token_map, map_len, params,
+                                             codes, scales, w.idx, w.mem, err_flags, stream),
+                  "engram_precompute: hash + gather");
+    if (rc != ENGRAM_OK) return rc;
+    if ((rc = mark(1)) != ENGRAM_OK) return rc;
+  } else if (T > 0) {
+    rc = from_hip(engram::launch_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, params, w.idx,
+                                      err_flags, stream),
+                  "engram_precompute: hash");
+    if (rc != ENGRAM_OK) return rc;
+    if (packed) {
+      // Only live (non-DEAD) positions are decoded and projected: a DEAD
+      // position passes through the gate untouched, so its k/v are never
+      // read. Their mem and kv rows are packed in position order, slot[t]
+      // locating position t's and live_pos[i] the position of row i; the
+      // projection and the gate read the live count on the device.
+      rc = from_hip(engram::launch_live_slots(tok, T, w.slot, w.live, w.live + 1, w.live_pos, stream),
+                    "engram_precompute: live slots");
+      if (rc != ENGRAM_OK) return rc;
+    }
+    if ((rc = mark(1)) != ENGRAM_OK) return rc;
+    if (stage) {
+      rc = from_hip(engram::launch_stage_rows(w.idx, T, codes, scales, params.n_rows, w.stage_codes,
+                                              w.stage_scales, err_flags, stream),
+                    "engram_precompute: stage rows");
+      if (rc != ENGRAM_OK) return rc;
+    }
+    rc = from_hip(engram::launch_gather_decode(w.idx, T, stage ? w.stage_codes : codes,
+                                               stage ? w.stage_scales : scales, params.n_rows, w.mem,
+                                               slot, stage, err_flags, stream),
+                  "engram_precompute: gather + decode");
+    if (rc != ENGRAM_OK) return rc;
+  } else if ((rc = mark(1)) != ENGRAM_OK) {
+    return rc;
+  }
+  if ((rc = mark(2)) != ENGRAM_OK) return rc;
+  rc = from_hip(engram::launch_project(w.mem, T, packed ? w.live : nullptr, wkv, wkv_packed, (hc + 1) * H,
+                                       w.kv, stream),
+                "engram_precompute: project");
+  if (rc != ENGRAM_OK) return rc;
+  return mark(3);
+}
+
+// Host checks of engram_gate_precomputed's arguments.
+int check_gate_precomputed_args(const uint16_t* hidden, const void* ws, size_t ws_bytes,
+                                const uint32_t* tok, int32_t S, int64_t T, const float* wqk,
+                                int32_t H, int32_t hc, float eps, const float* gate_out) {
+  int rc = check_dims(H, hc);
+  if (rc != ENGRAM_OK) return rc;
+  if (S < 0) return fail(ENGRAM_EINVAL, "S < 0");
+  if (T > 0) {
+    const size_t need = engram_forward_workspace(T, H, hc);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(ENGRAM_EINVAL, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (!aligned(ws, 256)) return fail(ENGRAM_EINVAL, "workspace must be 256-byte aligned");
+    if (tok == nullptr) return fail(ENGRAM_EINVAL, "tok is NULL");
+    if (S == 0) return fail(ENGRAM_EINVAL, "T = %lld tokens but S = 0 sequences", (long long)T);
+  }
+  const engram::WorkspaceLayout w = engram::workspace_layout(const_cast<void*>(ws), T > 0 ? T : 0, H, hc);
+  return check_gate_args(hidden, w.kv, wqk, tok, T, H, hc, eps, gate_out);
+}
+
+int enqueue_gate_precomputed(uint16_t* hidden, const void* ws, const uint32_t* tok, int32_t S,
+                             int64_t T, const float* wqk, int32_t H, int32_t hc, float eps,
+                             float dot_scale, float* gate_out, hipStream_t stream) {
+  const engram::WorkspaceLayout w = engram::workspace_layout(const_cast<void*>(ws), T, H, hc);
+  const bool packed = engram::packs_rows(T, S);
+  return from_hip(engram::launch_gate(hidden, w.kv, wqk, tok, packed ? w.slot : nullptr,
+                                      packed ? w.live_pos : nullptr, packed ? w.live : nullptr, T, H,
+                                      hc, eps, dot_scale, gate_out, stream),
+                  "engram_gate_precomputed");
+}
+
 }  // namespace
+
+namespace engram {
+
+int report(int status, const char* what, hipError_t e) {
+  if (e != hipSuccess) return fail(status, "%s: %s", what, hipGetErrorString(e));
+  return fail(status, "%s", what);
+}
+
+int forward_impl(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                 const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                 const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,
+                 const uint16_t* wkv, const uint16_t* wkv_packed, const float* wqk, uint16_t* hidden,
+                 int32_t H, int32_t hc, float eps, float dot_scale, void* ws, size_t ws_bytes,
+                 float* gate_out, uint32_t* err_flags, hipEvent_t* stage_events, hipStream_t stream) {
+  // Every stage's arguments are checked before anything is enqueued.
+  int rc = check_precompute_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, codes, scales,
+                                 wkv, wkv_packed, H, hc, 0, ws, ws_bytes);
+  if (rc != ENGRAM_OK) return rc;
+  if ((rc = check_gate_precomputed_args(hidden, ws, ws_bytes, tok, S, T, wqk, H, hc, eps, gate_out)) !=
+      ENGRAM_OK)
+    return rc;
+  rc = enqueue_precompute(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, codes, scales, wkv,
+                          wkv_packed, H, hc, 0, ws, err_flags, stage_events, stream);
+  if (rc != ENGRAM_OK) return rc;
+  rc = enqueue_gate_precomputed(hidden, ws, tok, S, T, wqk, H, hc, eps, dot_scale, gate_out, stream);
+  if (rc != ENGRAM_OK) return rc;
+  if (stage_events != nullptr)
+    return from_hip(hipEventRecord(stage_events[4], stream), "engram_forward: hipEventRecord");
+  return ok();
+}
+
+}  // namespace engram
 
 extern "C" {
 
@@ -253,7 +402,7 @@ int engram_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                          uint32_t* err_flags, hipStream_t stream) {
   const int rc = check_gather_args(idx, T, codes, scales, n_rows, mem);
   if (rc != ENGRAM_OK) return rc;
-  return from_hip(engram::launch_gather_decode(idx, T, codes, scales, n_rows, mem, nullptr, err_flags,
+  return from_hip(engram::launch_gather_decode(idx, T, codes, scales, n_rows, mem, nullptr, false, err_flags,
                                                 stream),
                   "engram_gather_decode");
 }
@@ -291,10 +440,28 @@ int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const ui
 
 size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc) {
   if (T <= 0 || H <= 0 || hc <= 0) return 0;
-  const size_t t = (size_t)T;
-  return round256(t * ENGRAM_BUCKETS * 4) + round256(t * 4) +
-         round256(4 * (1 + (size_t)engram::live_chunks(T))) + round256(t * ENGRAM_MEM * 2) +
-         round256(t * (size_t)(hc + 1) * (size_t)H * 2) + round256(t * 4);
+  return engram::workspace_layout(nullptr, T, H, hc).bytes;
+}
+
+int engram_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                      const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                      const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,
+                      const uint16_t* wkv, const uint16_t* wkv_packed, int32_t H, int32_t hc,
+                      uint32_t flags, void* ws, size_t ws_bytes, uint32_t* err_flags,
+                      hipStream_t stream) {
+  const int rc = check_precompute_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, codes,
+                                       scales, wkv, wkv_packed, H, hc, flags, ws, ws_bytes);
+  if (rc != ENGRAM_OK) return rc;
+  return enqueue_precompute(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, codes, scales,
+                            wkv, wkv_packed, H, hc, flags, ws, err_flags, nullptr, stream);
+}
+
+int engram_gate_precomputed(uint16_t* hidden, const void* ws, size_t ws_bytes, const uint32_t* tok,
+                            int32_t S, int64_t T, const float* wqk, int32_t H, int32_t hc,
+                            float eps, float dot_scale, float* gate_out, hipStream_t stream) {
+  const int rc = check_gate_precomputed_args(hidden, ws, ws_bytes, tok, S, T, wqk, H, hc, eps, gate_out);
+  if (rc != ENGRAM_OK) return rc;
+  return enqueue_gate_precomputed(hidden, ws, tok, S, T, wqk, H, hc, eps, dot_scale, gate_out, stream);
 }
 
 int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
@@ -304,88 +471,9 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
                    uint16_t* hidden, int32_t H, int32_t hc, float eps, float dot_scale, void* ws,
                    size_t ws_bytes, float* gate_out, uint32_t* err_flags,
                    hipEvent_t* stage_events, hipStream_t stream) {
-  int rc = check_dims(H, hc);
-  if (rc != ENGRAM_OK) return rc;
-  const size_t need = engram_forward_workspace(T, H, hc);
-  if (T > 0) {
-    if (ws == nullptr || ws_bytes < need)
-      return fail(ENGRAM_EINVAL, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    if (!aligned(ws, 256)) return fail(ENGRAM_EINVAL, "workspace must be 256-byte aligned");
-  }
-  // Workspace: idx [T][24] | slot [T] | live count + per-chunk counts |
-  // mem | kv | live positions [T], each section 256-byte aligned.
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  const size_t t = T > 0 ? (size_t)T : 0;
-  const size_t o_slot = round256(t * ENGRAM_BUCKETS * 4), o_count = o_slot + round256(t * 4);
-  const size_t o_mem = o_count + round256(4 * (1 + (size_t)engram::live_chunks((int64_t)t)));
-  const size_t o_kv = o_mem + round256(t * ENGRAM_MEM * 2);
-  const size_t o_pos = o_kv + round256(t * (size_t)(hc + 1) * (size_t)H * 2);
-  uint32_t* idx = reinterpret_cast<uint32_t*>(w);
-  uint32_t* live_pos = reinterpret_cast<uint32_t*>(w + o_pos);
-  uint32_t* slot = reinterpret_cast<uint32_t*>(w + o_slot);
-  uint32_t* live = reinterpret_cast<uint32_t*>(w + o_count);
-  uint16_t* mem = reinterpret_cast<uint16_t*>(w + o_mem);
-  uint16_t* kv = reinterpret_cast<uint16_t*>(w + o_kv);
-  // Every stage's arguments are checked before anything is enqueued.
-  if ((rc = check_hash_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params, idx)) != ENGRAM_OK ||
-      (rc = check_gather_args(idx, T, codes, scales, params->n_rows, mem)) != ENGRAM_OK ||
-      (rc = check_project_args(mem, T, wkv, wkv_packed, H, hc, kv)) != ENGRAM_OK ||
-      (rc = check_gate_args(hidden, kv, wqk, tok, T, H, hc, eps, gate_out)) != ENGRAM_OK)
-    return rc;
-  auto mark = [&](int i) -> int {
-    if (stage_events == nullptr) return ENGRAM_OK;
-    return from_hip(hipEventRecord(stage_events[i], stream), "engram_forward: hipEventRecord");
-  };
-  if ((rc = mark(0)) != ENGRAM_OK) return rc;
-  if (T == 0 || (T <= engram::kHashGatherMaxTokens && S <= engram::kHashGatherMaxSeqs)) {
-    // Small batch: one kernel hashes, gathers and decodes; stage events 1
-    // and 2 both mark its end.
-    if (T > 0) {
-      rc = from_hip(engram::launch_hash_gather(tok, cu_seqlens, S, T, hist, token_map, map_len,
-                                               *params, codes, scales, idx, mem, err_flags, stream),
-                    "engram_forward: hash + gather");
-      if (rc != ENGRAM_OK) return rc;
-    }
-    if ((rc = mark(1)) != ENGRAM_OK) return rc;
-    if ((rc = mark(2)) != ENGRAM_OK) return rc;
-    rc = from_hip(engram::launch_project(mem, T, nullptr, wkv, wkv_packed, (hc + 1) * H, kv, stream),
-                  "engram_forward: project");
-    if (rc != ENGRAM_OK) return rc;
-    if ((rc = mark(3)) != ENGRAM_OK) return rc;
-    rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, nullptr, nullptr, nullptr, T, H, hc, eps,
-                                      dot_scale, gate_out, stream),
-                  "engram_forward: gate");
-    if (rc != ENGRAM_OK) return rc;
-    return mark(4);
-  }
-  // Larger batches: only live (non-DEAD) positions are decoded and projected.
-  // DEAD positions pass through the gate untouched, so their k/v are never
-  // read; the live rows of mem and kv are packed in position order, slot[t]
-  // locating position t's and live_pos[i] the position of row i, and the
-  // projection and the gate read the live count on the device, so nothing
-  // waits on the host.
-  rc = from_hip(engram::launch_hash(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, idx,
-                                    err_flags, stream),
-                "engram_forward: hash");
-  if (rc != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_live_slots(tok, T, slot, live, live + 1, live_pos, stream),
-                "engram_forward: live slots");
-  if (rc != ENGRAM_OK) return rc;
-  if ((rc = mark(1)) != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_gather_decode(idx, T, codes, scales, params->n_rows, mem, slot,
-                                             err_flags, stream),
-                "engram_forward: gather + decode");
-  if (rc != ENGRAM_OK) return rc;
-  if ((rc = mark(2)) != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_project(mem, T, live, wkv, wkv_packed, (hc + 1) * H, kv, stream),
-                "engram_forward: project");
-  if (rc != ENGRAM_OK) return rc;
-  if ((rc = mark(3)) != ENGRAM_OK) return rc;
-  rc = from_hip(engram::launch_gate(hidden, kv, wqk, tok, slot, live_pos, live, T, H, hc, eps,
-                                    dot_scale, gate_out, stream),
-                "engram_forward: gate");
-  if (rc != ENGRAM_OK) return rc;
-  return mark(4);
+  return engram::forward_impl(tok, cu_seqlens, S, T, hist, token_map, map_len, params, codes, scales,
+                              wkv, wkv_packed, wqk, hidden, H, hc, eps, dot_scale, ws, ws_bytes,
+                              gate_out, err_flags, stage_events, stream);
 }
 
 int engram_gen_table(uint8_t* codes, uint8_t* scales, uint64_t row_begin, uint64_t n_rows,

@@ -32,9 +32,19 @@ hipError_t launch_live_slots(const uint32_t* tok, int64_t T, uint32_t* slot, uin
                              uint32_t* chunk_count, uint32_t* live_pos, hipStream_t st);
 // slot: NULL (position t's rows go to mem row t), or the live_slots map
 // (they go to row slot[t]; DEAD positions write nothing).
+// staged: codes/scales are launch_stage_rows' staging area, where row
+// t*24 + j holds table row idx[t][j] (idx still marks DEAD and out-of-range
+// rows); otherwise they are the table and row idx[t][j] is read.
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                                 const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
-                                const uint32_t* slot, uint32_t* err, hipStream_t st);
+                                const uint32_t* slot, bool staged, uint32_t* err, hipStream_t st);
+// Copies table row idx[t][j] (256 code bytes, 8 scale bytes) to row t*24 + j
+// of a staging area in device memory, for tables in pinned host memory:
+// every row crosses the host link once, in 16-byte loads with many rows in
+// flight. DEAD and out-of-range rows are skipped (the latter flagged).
+hipError_t launch_stage_rows(const uint32_t* idx, int64_t T, const uint8_t* codes,
+                             const uint8_t* scales, uint64_t n_rows, uint8_t* stage_codes,
+                             uint8_t* stage_scales, uint32_t* err, hipStream_t st);
 // Hash, gather and decode as one kernel (hash_gather.hip): for batches of at
 // most kHashGatherMaxTokens tokens in at most kHashGatherMaxSeqs sequences,
 // where both steps are latency-bound chains of loads. Writes the same idx and
@@ -100,6 +110,67 @@ inline hipError_t cu_count(int* n) {
   *n = c;
   return hipSuccess;
 }
+
+// Batches above these limits pack the live positions' rows (see launch_live_slots).
+inline bool packs_rows(int64_t T, int32_t S) {
+  return T > kHashGatherMaxTokens || S > kHashGatherMaxSeqs;
+}
+
+// Sections of the per-layer workspace, each 256-byte aligned:
+//   idx uint32[T][24] | slot uint32[T] | live count + per-chunk counts |
+//   mem bf16[T][6144] | kv bf16[T][(hc+1)H] | live positions uint32[T].
+// The kv section is at least T*24*264 bytes: rows staged from a host table
+// (codes [T*24][256], then scales [T*24][8]) sit there until the decode has
+// read them, before the projection writes kv.
+struct WorkspaceLayout {
+  size_t bytes;
+  uint32_t* idx;
+  uint32_t* slot;
+  uint32_t* live;
+  uint16_t* mem;
+  uint16_t* kv;
+  uint32_t* live_pos;
+  uint8_t* stage_codes;
+  uint8_t* stage_scales;
+};
+
+inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WorkspaceLayout workspace_layout(void* ws, int64_t T, int32_t H, int32_t hc) {
+  const size_t t = T > 0 ? (size_t)T : 0;
+  const size_t kv_bytes = t * (size_t)(hc + 1) * (size_t)H * 2;
+  const size_t stage_bytes = t * ENGRAM_BUCKETS * (ENGRAM_ROW + ENGRAM_SCALES_PER_ROW);
+  const size_t o_slot = round256(t * ENGRAM_BUCKETS * 4);
+  const size_t o_count = o_slot + round256(t * 4);
+  const size_t o_mem = o_count + round256(4 * (1 + (size_t)live_chunks((int64_t)t)));
+  const size_t o_kv = o_mem + round256(t * ENGRAM_MEM * 2);
+  const size_t o_pos = o_kv + round256(kv_bytes > stage_bytes ? kv_bytes : stage_bytes);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  WorkspaceLayout L;
+  L.bytes = o_pos + round256(t * 4);
+  L.idx = reinterpret_cast<uint32_t*>(w);
+  L.slot = reinterpret_cast<uint32_t*>(w + o_slot);
+  L.live = reinterpret_cast<uint32_t*>(w + o_count);
+  L.mem = reinterpret_cast<uint16_t*>(w + o_mem);
+  L.kv = reinterpret_cast<uint16_t*>(w + o_kv);
+  L.live_pos = reinterpret_cast<uint32_t*>(w + o_pos);
+  L.stage_codes = w + o_kv;
+  L.stage_scales = w + o_kv + t * ENGRAM_BUCKETS * ENGRAM_ROW;
+  return L;
+}
+
+// The body of engram_forward, argument checks included (engram_api.cpp); the
+// entry point without a workspace argument calls it with its own device buffer.
+int forward_impl(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                 const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                 const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,
+                 const uint16_t* wkv, const uint16_t* wkv_packed, const float* wqk, uint16_t* hidden,
+                 int32_t H, int32_t hc, float eps, float dot_scale, void* ws, size_t ws_bytes,
+                 float* gate_out, uint32_t* err_flags, hipEvent_t* stage_events, hipStream_t stream);
+
+// Sets this thread's engram_last_error() text (with the HIP error's name when
+// e != hipSuccess) and returns status.
+int report(int status, const char* what, hipError_t e);
 
 // ---------------------------------------------------------------- device helpers
 // float32 -> bfloat16 bits, round to nearest even (gfx950 converts in hardware).

@@ -29,7 +29,7 @@ constexpr int kRowsInFlight = 4;         // passes per workgroup (rows per lane)
 __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
     const uint32_t* __restrict__ idx, int64_t total_rows, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, uint64_t n_rows, uint16_t* __restrict__ mem,
-    const uint32_t* __restrict__ slot, uint32_t* err) {
+    const uint32_t* __restrict__ slot, bool staged, uint32_t* err) {
   const int l = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;
   const int64_t base = (int64_t)blockIdx.x * (kGroups * kRowsInFlight);
@@ -60,10 +60,11 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
       if (row != ENGRAM_DEAD_IDX) {
         if ((uint64_t)row < n_rows) {
           live[u] = true;
-          const uint8_t* cr = codes + (uint64_t)row * ENGRAM_ROW;
+          const uint64_t src = staged ? (uint64_t)r : (uint64_t)row;
+          const uint8_t* cr = codes + src * ENGRAM_ROW;
           ca[u] = *reinterpret_cast<const uint2*>(cr + l * 8);
           cb[u] = *reinterpret_cast<const uint2*>(cr + 128 + l * 8);
-          const uint2 s2 = *reinterpret_cast<const uint2*>(scales + (uint64_t)row * ENGRAM_SCALES_PER_ROW);
+          const uint2 s2 = *reinterpret_cast<const uint2*>(scales + src * ENGRAM_SCALES_PER_ROW);
           sa[u] = (s2.x >> sh) & 0xFFu;
           sb[u] = (s2.y >> sh) & 0xFFu;
         } else {
@@ -79,16 +80,74 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
   }
 }
 
+// Staging copy for tables in pinned host memory: a 16-lane group moves one
+// 256-byte row with one 16-byte load per lane (lane 0 also moves the row's
+// 8 scale bytes), kStageRowsInFlight rows per lane outstanding, since every
+// read crosses the host link and waits on its latency.
+constexpr int kStageRowsInFlight = 8;
+
+__global__ __launch_bounds__(kBlock) void stage_rows_kernel(
+    const uint32_t* __restrict__ idx, int64_t total_rows, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, uint64_t n_rows, uint8_t* __restrict__ stage_codes,
+    uint8_t* __restrict__ stage_scales, uint32_t* err) {
+  const int l = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;
+  const int64_t base = (int64_t)blockIdx.x * (kGroups * kStageRowsInFlight);
+  uint4 c[kStageRowsInFlight];
+  uint2 sc[kStageRowsInFlight];
+  bool go[kStageRowsInFlight];
+#pragma unroll
+  for (int u = 0; u < kStageRowsInFlight; ++u) {
+    const int64_t r = base + u * kGroups + grp;
+    go[u] = false;
+    c[u] = make_uint4(0, 0, 0, 0);
+    sc[u] = make_uint2(0, 0);
+    if (r < total_rows) {
+      const uint32_t row = idx[r];
+      if (row != ENGRAM_DEAD_IDX) {
+        if ((uint64_t)row < n_rows) {
+          go[u] = true;
+          c[u] = *reinterpret_cast<const uint4*>(codes + (uint64_t)row * ENGRAM_ROW + l * 16);
+          if (l == 0)
+            sc[u] = *reinterpret_cast<const uint2*>(scales + (uint64_t)row * ENGRAM_SCALES_PER_ROW);
+        } else {
+          set_err(err, ENGRAM_ERR_ROW_RANGE);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kStageRowsInFlight; ++u) {
+    if (!go[u]) continue;
+    const int64_t r = base + u * kGroups + grp;
+    *reinterpret_cast<uint4*>(stage_codes + r * ENGRAM_ROW + l * 16) = c[u];
+    if (l == 0) *reinterpret_cast<uint2*>(stage_scales + r * ENGRAM_SCALES_PER_ROW) = sc[u];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stage_rows(const uint32_t* idx, int64_t T, const uint8_t* codes,
+                             const uint8_t* scales, uint64_t n_rows, uint8_t* stage_codes,
+                             uint8_t* stage_scales, uint32_t* err, hipStream_t st) {
+  const int64_t rows = T * ENGRAM_BUCKETS;
+  if (rows == 0) return hipSuccess;
+  const int64_t per_block = (int64_t)kGroups * kStageRowsInFlight;
+  const unsigned blocks = (unsigned)((rows + per_block - 1) / per_block);
+  stage_rows_kernel<<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, stage_codes,
+                                               stage_scales, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                                 const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
-                                const uint32_t* slot, uint32_t* err, hipStream_t st) {
+                                const uint32_t* slot, bool staged, uint32_t* err, hipStream_t st) {
   const int64_t rows = T * ENGRAM_BUCKETS;
   if (rows == 0) return hipSuccess;
   const int64_t per_block = (int64_t)kGroups * kRowsInFlight;
   const unsigned blocks = (unsigned)((rows + per_block - 1) / per_block);
-  gather_decode_kernel<<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, mem, slot, err);
+  gather_decode_kernel<<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, mem, slot, staged,
+                                                  err);
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 2
+#define ENGRAM_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 #define ENGRAM_OK            0
@@ -208,18 +208,65 @@ int engram_gate(uint16_t* hidden, const uint16_t* kv, const float* wqk, const ui
 
 /* ---------------------------------------------------------------- whole layer */
 
-/* Workspace bytes engram_forward needs for T tokens. Layout, each section
- * 256-byte aligned: idx uint32[T][24] | slot uint32[T] | live count uint32
- * and one uint32 per 4,096 positions | mem bf16[T][6144] | kv
- * bf16[T][(hc+1)*H] | live positions uint32[T] (position of each packed
- * row, for batches above the small-batch limits). */
+/* Workspace bytes engram_forward (and engram_precompute) needs for T
+ * tokens. Layout, each section 256-byte aligned: idx uint32[T][24] | slot
+ * uint32[T] | live count uint32 and one uint32 per 4,096 positions | mem
+ * bf16[T][6144] | kv bf16[T][(hc+1)*H] (at least T*24*264 bytes: rows staged
+ * from a host table sit there until they are decoded) | live positions
+ * uint32[T] (position of each packed row, for batches above the small-batch
+ * limits). */
 size_t engram_forward_workspace(int64_t T, int32_t H, int32_t hc);
 
-/* One Engram layer: engram_hash -> engram_gather_decode -> engram_project ->
- * engram_gate, enqueued on one stream, intermediates in `ws` (caller-owned
- * device memory of at least engram_forward_workspace(T, H, hc) bytes,
- * 256-byte aligned). Arguments mean what they mean in the stage calls, and
- * every stage's host checks run before anything is enqueued (an
+/* engram_precompute flag: copy the selected rows and scales into the
+ * workspace first (16-byte loads, many rows in flight), then decode them
+ * from device memory; for tables in pinned host memory ([vLLM] CPU offload:
+ * host-resident tables whose rows are fetched ahead of use). Without it the
+ * decode reads the table in place. The results are the same either way. */
+#define ENGRAM_PRECOMPUTE_STAGE_ROWS 0x1u
+
+/* The half of one Engram layer that does not read the hidden state:
+ * engram_hash -> engram_gather_decode -> engram_project, into `ws`
+ * (caller-owned device memory of at least engram_forward_workspace(T, H, hc)
+ * bytes, 256-byte aligned). Only the gate needs the layer's input hidden
+ * state, so this can run ahead of the layer, e.g. on a side stream while the
+ * layers before it run ([zLLM] 提前投影: the projection is issued before the
+ * layer is reached and only the gate waits for the hidden state; [FlagOS]
+ * 4.1: the lookup is prefetched and overlapped with compute).
+ * Arguments mean what they mean in the stage calls; every host check runs
+ * before anything is enqueued; the library allocates nothing. `hist` is read
+ * only and must hold the history before this step (call
+ * engram_history_append once per step, after every layer's precompute has
+ * been enqueued on, or ordered before, the append's stream).
+ * flags: 0 or ENGRAM_PRECOMPUTE_STAGE_ROWS.
+ * For T <= 1024 tokens in S <= 1024 sequences, mem/kv row t belongs to
+ * position t (hash, gather and decode run as one kernel unless rows are
+ * staged). Larger batches decode and project only the live (non-DEAD)
+ * positions, packed in position order: slot[t] is the row of position t
+ * or ENGRAM_DEAD_IDX, and the live count is read on the device.
+ * The workspace then holds everything engram_gate_precomputed reads. */
+int engram_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                      const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                      const engram_hash_params* params, const uint8_t* codes, const uint8_t* scales,
+                      const uint16_t* wkv, const uint16_t* wkv_packed, int32_t H, int32_t hc,
+                      uint32_t flags, void* ws, size_t ws_bytes, uint32_t* err_flags,
+                      hipStream_t stream);
+
+/* The gate at layer entry ([zLLM] 提前投影: only the gate reads the layer's
+ * hidden state): engram_gate on hidden[T][hc][H] with the keys and value
+ * that engram_precompute left in `ws` for the same tok, S, T, H and hc
+ * (anything else is undefined: the workspace layout depends on T and S).
+ * DEAD positions pass through bit-identical with gate 0. The precompute must
+ * be complete or ordered before this call on `stream` (an event wait when it
+ * ran on another stream). Requires tok (the DEAD mask) for T > 0. */
+int engram_gate_precomputed(uint16_t* hidden, const void* ws, size_t ws_bytes, const uint32_t* tok,
+                            int32_t S, int64_t T, const float* wqk, int32_t H, int32_t hc,
+                            float eps, float dot_scale, float* gate_out, hipStream_t stream);
+
+/* One Engram layer: engram_precompute (flags 0) followed by
+ * engram_gate_precomputed, enqueued on one stream with intermediates in `ws`
+ * (caller-owned device memory of at least engram_forward_workspace(T, H, hc)
+ * bytes, 256-byte aligned). Arguments mean what they mean in the stage
+ * calls, and every stage's host checks run before anything is enqueued (an
  * ENGRAM_EINVAL return leaves the stream untouched).
  * Per step: call once per layer with that layer's params/table/wkv/wqk and
  * hidden, all reading the same `hist`, then engram_history_append once.

@@ -61,6 +61,26 @@ def assert_bf16_close(got: np.ndarray, ref: np.ndarray, rel: float = 2e-2, what:
                              f"{tuple(i)}: got {g[tuple(i)]!r} ref {r[tuple(i)]!r}")
 
 
+def check_gate_rows(got_h, got_g, hidden, got_kv, ref_kv, wqk, dead, H, hc, dot_scale, what):
+    """Hidden and gate of the given rows. End to end: hidden against the
+    oracle's gate + residual on the oracle's k/v (ref_kv; None to skip).
+    On identical inputs: hidden and gate against the oracle's gate +
+    residual on the kernel's own k/v (got_kv), the gate at every position.
+    (End to end the gate inherits k's BF16 rounding: a key element whose
+    float32 and float64 sums round to neighbouring BF16 values moves dot by
+    about 1e-2, which near dot = 0 moves sqrt(|dot|), and the gate, by more
+    than 1e-3; so the gate bar is applied where its inputs are the same.)"""
+    got_kv = np.where(dead[:, None], 0, got_kv)          # DEAD rows have no k/v; their gate is skipped
+    new, g, _ = O.gate_residual(hidden, got_kv, wqk, dead, H, hc, 1e-6, dot_scale)
+    assert_bf16_close(got_h.reshape(-1, H), new.reshape(-1, H), what=f"{what} hidden (same k/v)")
+    assert np.max(np.abs(got_g - g), initial=0.0) <= 1e-3, what
+    if ref_kv is not None:
+        new_ref, _, _ = O.gate_residual(hidden, ref_kv, wqk, dead, H, hc, 1e-6, dot_scale)
+        assert_bf16_close(got_h.reshape(-1, H), new_ref.reshape(-1, H), what=f"{what} hidden (end to end)")
+    assert np.array_equal(got_h[dead], hidden[dead])
+    assert np.all(got_g[dead] == 0)
+
+
 @dataclasses.dataclass
 class World:
     """Host inputs of one config and layer (small enough to hold on the host)."""
@@ -144,7 +164,8 @@ def live_positions(ws: torch.Tensor, T: int, H: int, hc: int):
     """Device view of the workspace's last section: the position of each packed
     (live) row, in row order, for batches that pack rows."""
     r = lambda x: (x + 255) // 256 * 256
-    o_pos = r(T * 96) + r(T * 4) + r(4 * (1 + (T + 4095) // 4096)) + r(T * 12288) + r(T * (hc + 1) * H * 2)
+    kv_section = r(max(T * (hc + 1) * H * 2, T * 24 * 264))   # also holds rows staged from a host table
+    o_pos = r(T * 96) + r(T * 4) + r(4 * (1 + (T + 4095) // 4096)) + r(T * 12288) + kv_section
     return ws[o_pos: o_pos + T * 4].view(torch.int32)
 
 

@@ -31,7 +31,7 @@ def test_header_declares_the_stage_entry_points():
     for n in ("engram_hash", "engram_gather_decode", "engram_project", "engram_gate",
               "engram_forward", "engram_history_append", "engram_history_fork",
               "engram_history_reset", "engram_check_params", "engram_forward_workspace",
-              "engram_pack_wkv"):
+              "engram_pack_wkv", "engram_precompute", "engram_gate_precomputed"):
         assert n in names
 
 
@@ -43,7 +43,8 @@ def test_library_exports_every_declared_symbol(E):
     assert not missing, missing
     for n in _declared():
         assert hasattr(E.lib, n)
-    assert E.lib.engram_abi_version() == 2
+    header_version = int(re.search(r"#define ENGRAM_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert E.lib.engram_abi_version() == header_version
 
 
 def test_status_strings(E):
@@ -163,6 +164,46 @@ def test_forward_checks_its_stage_arguments_on_both_paths(E):
                             None) == 0
 
 
+def test_precompute_and_gate_precomputed_check_arguments_before_launch(E):
+    """The split layer (hidden-independent precompute, then the gate at layer
+    entry) applies the same host checks as engram_forward before any launch;
+    none of these calls reaches a device."""
+    L = E.lib
+    p, _ = _params()
+    fake = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x100000)
+    H, hc = 256, 4
+    for S, T in ((1, 8), (1, 2000)):
+        need = L.engram_forward_workspace(T, H, hc)
+        def pre(hp, flags=0, ws_bytes=need, w=ws, codes=fake):
+            return L.engram_precompute(fake, fake, S, T, fake, fake, 10, ctypes.byref(hp), codes, fake,
+                                       fake, None, H, hc, flags, w, ws_bytes, None, None)
+        hp = E.HashParams.from_any(p)
+        assert pre(hp, ws_bytes=need - 1) == -1 and b"workspace" in L.engram_last_error()
+        assert pre(hp, w=ctypes.c_void_p(0x100010)) == -1 and b"256-byte" in L.engram_last_error()
+        assert pre(hp, flags=0x2) == -1 and b"flags" in L.engram_last_error()
+        assert pre(hp, codes=ctypes.c_void_p(0x10008)) == -1
+        bad = E.HashParams.from_any(p)
+        bad.prime[3] = 9
+        assert pre(bad) == -1
+        def gate(ws_bytes=need, tok=fake, S=S, wqk=fake, hidden=fake):
+            return L.engram_gate_precomputed(hidden, ws, ws_bytes, tok, S, T, wqk, H, hc, 1e-6, 1.0,
+                                             None, None)
+        assert gate(ws_bytes=need - 1) == -1 and b"workspace" in L.engram_last_error()
+        assert gate(tok=None) == -1
+        assert gate(S=0) == -1
+        assert gate(wqk=ctypes.c_void_p(0x10004)) == -1
+        assert gate(hidden=None) == -1
+        assert L.engram_gate_precomputed(fake, ws, need, fake, S, T, fake, 100, hc, 1e-6, 1.0, None,
+                                         None) == -1                   # H % 64
+    # no tokens: nothing to launch, succeeds without a device
+    hp = E.HashParams.from_any(p)
+    assert L.engram_precompute(None, fake, 1, 0, None, None, 0, ctypes.byref(hp), None, None, None,
+                               None, H, hc, 0, None, 0, None, None) == 0
+    assert L.engram_gate_precomputed(None, None, 0, None, 1, 0, None, H, hc, 1e-6, 1.0, None,
+                                     None) == 0
+
+
 def test_pack_wkv_rejects_bad_arguments_before_launch(E):
     """engram_pack_wkv checks shapes, pointers, alignment and overlap on the
     host; none of these calls reaches a device."""
@@ -186,6 +227,11 @@ def test_workspace_size_formula(E):
         assert E.engram_forward_workspace(T, H, hc) == (r(T * 96) + r(T * 4) + r(4 * (1 + (T + 4095) // 4096))
                                                         + r(T * 12288) + r(T * 25600 * 2) + r(T * 4))
     assert E.engram_forward_workspace(0, H, hc) == 0
+    # narrow layers: the kv section still holds the rows staged from a host table
+    for T, H, hc in ((64, 256, 4), (3, 64, 1)):
+        assert E.engram_forward_workspace(T, H, hc) == (r(T * 96) + r(T * 4) + r(4 * (1 + (T + 4095) // 4096))
+                                                        + r(T * 12288) + r(max(T * (hc + 1) * H * 2, T * 24 * 264))
+                                                        + r(T * 4))
 
 
 def test_table_pointers_accept_pinned_host_memory_only(E):

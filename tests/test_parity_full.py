@@ -15,7 +15,8 @@ import torch
 import engram_synth as synth
 from oracle import engram_oracle as O
 from tests.conftest import gpu_available
-from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, down32,
+from tests.gpu_helpers import (DEV, World, assert_bf16_close, check_gate_rows, device_table, down16,
+                               down32,
                                forward_rows, hidden_device, hidden_rows, log, up16, up32, upf, workspace_views)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow,
@@ -62,15 +63,11 @@ def _check_sampled(w, li, L, rows, idx_all, ws, T, S, hid_in, hid_out, gate_d, d
     ref_kv = O.project(ref_mem, L["wkv"])
     if has.any():
         assert_bf16_close(got_kv[has], ref_kv[has], what="kv")
-    new, g, dots = O.gate_residual(hid_in, ref_kv, L["wqk"], dead[rows], cfg.H, cfg.hc, 1e-6, 1.0)
     got_h = down16(hid_out).reshape(-1, cfg.hc, cfg.H)[rows]
-    assert_bf16_close(got_h.reshape(-1, cfg.H), new.reshape(-1, cfg.H), what="hidden")
-    assert np.array_equal(got_h[dead[rows]], hid_in[dead[rows]])
     got_g = gate_d.cpu().numpy().reshape(-1, cfg.hc)[rows]
-    well = np.abs(dots) >= 1e-2
-    assert np.max(np.abs(got_g - g)[well], initial=0.0) <= 1e-3
-    assert np.all(got_g[dead[rows]] == 0)
-    return int((~well).sum())
+    got_kv[~has] = 0
+    check_gate_rows(got_h, got_g, hid_in, got_kv, ref_kv, L["wqk"], dead[rows], cfg.H, cfg.hc, 1.0,
+                    "sampled rows")
 
 
 def _forward(E, w, li, L, tok_d, cu_d, hist_d, tmap_d, hidden_d, ws, T):
@@ -116,9 +113,7 @@ def test_full_size_one_layer(E):
     got_idx = down32(idx_d).reshape(T, 24)
     assert np.array_equal(got_idx, ref_idx)
     _ranges_ok(got_idx, dead, p)
-    n_small = _check_sampled(w, 0, L, rows, ref_idx, ws, T, len(cu) - 1, hid_in_rows, hidden_d, gate_d,
-                             dead)
-    log(f"  sampled gates with |dot| < 1e-2: {n_small}")
+    _check_sampled(w, 0, L, rows, ref_idx, ws, T, len(cu) - 1, hid_in_rows, hidden_d, gate_d, dead)
 
 
 def test_long_prefill_two_layers(E):
@@ -223,20 +218,28 @@ def test_multimodal_batched_decode(E):
     ws = torch.empty(E.engram_forward_workspace(S, cfg.H, cfg.hc), dtype=torch.uint8, device=DEV)
     dcu = np.arange(S + 1, dtype=np.int32)
     dcu_d = up32(dcu)
-    for step in range(4):
+    # all of the config's decode steps: indices and histories every step,
+    # sampled rows (decoded rows, k/v, hidden, gates) every 16th step
+    for step in range(cfg.decode_steps):
         dtok = synth.decode_tokens(cfg, step)
         dtok_d = up32(dtok)
         win, dead, h_out = O.walk(dtok, dcu, ref_hist, w.tmap, pad)
+        checked = step % 16 == 0 or step == cfg.decode_steps - 1
         for li in range(2):
             p = w.params[li]
-            hidden_d = hidden_device(cfg, cfg.layers[li], S, batch=100 + step)
-            rows = sorted(set([0, 1, 2, 127, 128, 255] + rng.integers(0, S, 4).tolist()))
-            hid_in_rows = hidden_rows(cfg, cfg.layers[li], rows, batch=100 + step)
+            hidden_d = (hidden_device(cfg, cfg.layers[li], S, batch=100 + step) if checked else
+                        torch.zeros((S, cfg.hc, cfg.H), dtype=torch.int16, device=DEV))
             gate_d = _forward(E, w, li, Ls[li], dtok_d, dcu_d, hist_all, tmap_d, hidden_d, ws, S)
             idx_d = workspace_views(ws, S, cfg.H, cfg.hc)[0]
             ref_idx = O.hash_windows(win, dead, p.mult, p.prime, p.offset)
             assert np.array_equal(down32(idx_d).reshape(S, 24), ref_idx), (step, li)
-            _check_sampled(w, li, Ls[li], rows, ref_idx, ws, S, S, hid_in_rows, hidden_d, gate_d, dead)
+            if checked:
+                rows = sorted(set([0, 1, 2, 127, 128, 255] + rng.integers(0, S, 4).tolist()))
+                hid_in_rows = hidden_rows(cfg, cfg.layers[li], rows, batch=100 + step)
+                _check_sampled(w, li, Ls[li], rows, ref_idx, ws, S, S, hid_in_rows, hidden_d, gate_d,
+                               dead)
         E.engram_history_append(hist_all, dtok_d, dcu_d, tmap_d, pad)
         ref_hist = h_out
         assert np.array_equal(down32(hist_all).reshape(S, 3), ref_hist)
+        if step % 32 == 31:
+            log(f"  decode step {step + 1} of {cfg.decode_steps}")

@@ -11,7 +11,8 @@ import torch
 import engram_synth as synth
 from oracle import engram_oracle as O
 from tests.conftest import gpu_available
-from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, down32, log,
+from tests.gpu_helpers import (DEV, World, assert_bf16_close, check_gate_rows, device_table, down16,
+                               down32, log,
                                forward_rows, up8, up16, up32, upf, workspace_views, live_positions)
 
 pytestmark = [pytest.mark.gpu,
@@ -418,15 +419,16 @@ def _run_forward(E, w, li, tok, cu, hist, hidden, dot_scale=1.0, packed=False):
                 gate=g_d.cpu().numpy().reshape(T, cfg.hc)), (wkv, wqk)
 
 
-def _check_forward(got, ref, hc, H):
+def _check_forward(got, ref, hc, H, hidden, wqk, dot_scale=1.0):
+    """idx and mem bit-exact, k/v within 2e-2; hidden end to end and, with the
+    gate, on the kernel's own k/v (check_gate_rows)."""
     assert np.array_equal(got["idx"], ref["idx"])
     assert np.array_equal(got["mem"], ref["mem"])
     assert_bf16_close(got["kv"], ref["kv"], what="kv")
     T = got["hidden"].shape[0]
     assert_bf16_close(got["hidden"].reshape(T * hc, H), ref["hidden"].reshape(T * hc, H), what="hidden")
-    well = np.abs(ref["dot"]) >= 1e-2
-    assert np.max(np.abs(got["gate"] - ref["gate"])[well]) <= 1e-3
-    return int((~well).sum())
+    check_gate_rows(got["hidden"], got["gate"], hidden, got["kv"], ref["kv"], wqk, ref["dead"], H, hc,
+                    dot_scale, "forward")
 
 
 @pytest.mark.parametrize("dot_scale", [1.0, 1 / 16.0])
@@ -440,8 +442,7 @@ def test_forward_tiny(E, dot_scale):
     got, (wkv, wqk) = _run_forward(E, w, 0, tok, cu, hist, hidden, dot_scale)
     ref = O.forward(tok, cu, hist, w.tmap, p, w.rows(0), wkv, wqk, hidden, cfg.H, cfg.hc,
                     1e-6, dot_scale)
-    n_small = _check_forward(got, ref, cfg.hc, cfg.H)
-    log(f"  gates with |dot| < 1e-2 (excluded from the gate bar): {n_small}")
+    _check_forward(got, ref, cfg.hc, cfg.H, hidden, wqk, dot_scale)
 
 
 def test_forward_is_deterministic(E):
@@ -471,10 +472,10 @@ def test_forward_decode_config(E):
     hidden = synth.hidden_bf16(cfg, 1, len(tok))
     got, (wkv, wqk) = _run_forward(E, w, 0, tok, cu, hist, hidden)
     ref = O.forward(tok, cu, hist, w.tmap, p, w.rows(0), wkv, wqk, hidden, cfg.H, cfg.hc)
-    _check_forward(got, ref, cfg.hc, cfg.H)
+    _check_forward(got, ref, cfg.hc, cfg.H, hidden, wqk)
     # the same step with wkv also passed in the packed decode layout
     got_p, _ = _run_forward(E, w, 0, tok, cu, hist, hidden, packed=True)
-    _check_forward(got_p, ref, cfg.hc, cfg.H)
+    _check_forward(got_p, ref, cfg.hc, cfg.H, hidden, wqk)
     for k in got:
         assert np.array_equal(got_p[k], got[k]), k
 
@@ -583,10 +584,9 @@ def test_forward_packs_live_rows_above_the_limits(E, H, hc):
     assert np.array_equal(got_mem[has], ref_mem[has])
     ref_kv = O.project(ref_mem, wkv)
     assert_bf16_close(got_kv[has], ref_kv[has], what="kv")
-    new, g, dots = O.gate_residual(hidden[rows], ref_kv, wqk, dead[rows], H, hc, 1e-6, 1.0)
-    assert_bf16_close(got_h[rows].reshape(-1, H), new.reshape(-1, H), what="hidden")
-    well = np.abs(dots) >= 1e-2
-    assert np.max(np.abs(got_g[rows] - g)[well], initial=0.0) <= 1e-3
+    got_kv[~has] = 0
+    check_gate_rows(got_h[rows], got_g[rows], hidden[rows], got_kv, ref_kv, wqk, dead[rows], H, hc, 1.0,
+                    "packed rows")
 
 
 def test_decode_steps_replayed_from_a_graph_match_eager(E):
@@ -638,94 +638,6 @@ def test_decode_steps_replayed_from_a_graph_match_eager(E):
         assert torch.equal(hist, ref[1]), r
         for i in range(steps):
             assert torch.equal(gates[i], ref[2][i]), (r, i)
-
-
-def test_two_layers_on_a_side_stream_match_one_stream(E):
-    """Running one layer's engram_forward on a side stream beside another's
-    (both read the same history; the append waits for both) gives the same
-    hidden states and history, bit for bit, as running them in turn on one
-    stream, over several decode steps."""
-    log("forward: two layers, side stream vs one stream, 3 decode steps")
-    w = World.of("decode")
-    cfg, p = w.cfg, w.params[0]
-    codes, scales = device_table(E, p.n_rows, *w.keys[0])
-    wkv = up16(synth.wkv_bf16(cfg, 1))
-    wqk = torch.from_numpy(synth.norm_weights(cfg, 1)).to(DEV)
-    tmap = up32(w.tmap)
-    S = cfg.n_seqs
-    cu = up32(np.arange(S + 1, dtype=np.int32))
-    ptok, pcu = synth.history_prefix_tokens(cfg)
-    toks = [up32(synth.decode_tokens(cfg, s)) for s in range(3)]
-    runs = []
-    for mode in ("one", "side"):
-        hist = torch.empty(S * 3, dtype=torch.int32, device=DEV)
-        E.engram_history_reset(hist, p.pad_cid)
-        E.engram_history_append(hist, up32(ptok), up32(pcu), tmap, p.pad_cid)
-        hidden = [up16(synth.hidden_bf16(cfg, layer, S)) for layer in (1, 2)]
-        ws = [torch.empty(E.engram_forward_workspace(S, cfg.H, cfg.hc), dtype=torch.uint8, device=DEV)
-              for _ in range(2)]
-        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
-        for tok in toks:
-            if mode == "side":
-                side.wait_stream(main)
-            for li in (1, 0):
-                st = side if (mode == "side" and li == 1) else main
-                E.engram_forward(tok, cu, hist, tmap, p, codes, scales, wkv, wqk, hidden[li],
-                                 cfg.H, cfg.hc, ws=ws[li], stream=st)
-            if mode == "side":
-                main.wait_stream(side)
-            E.engram_history_append(hist, tok, cu, tmap, p.pad_cid, stream=main)
-        torch.cuda.synchronize()
-        runs.append((down32(hist), [down16(h) for h in hidden]))
-    assert np.array_equal(runs[0][0], runs[1][0])
-    for a, b in zip(runs[0][1], runs[1][1]):
-        assert np.array_equal(a, b)
-
-
-def test_host_resident_table_matches_device_table(E):
-    """The decode config's 16M-row table in pinned host memory (mapped into
-    the device's address space; rows read across the host link) gives the
-    same gathered rows and the same decode step as the table in HBM."""
-    log("gather + forward: decode config with its table in pinned host memory")
-    w = World.of("decode")
-    cfg, p = w.cfg, w.params[0]
-    codes_h = torch.empty(p.n_rows * 256, dtype=torch.uint8, pin_memory=True)
-    scales_h = torch.empty(p.n_rows * 8, dtype=torch.uint8, pin_memory=True)
-    try:
-        E.engram_gen_table(codes_h, scales_h, 0, p.n_rows, *w.keys[0])
-    except E.EngramError as e:
-        pytest.skip(f"pinned host memory is not mapped for the device here: {e}")
-    codes_d, scales_d = device_table(E, p.n_rows, *w.keys[0])
-    torch.cuda.synchronize()
-    rows = np.random.default_rng(7).integers(0, p.n_rows, 64)
-    for r in rows:
-        assert torch.equal(codes_h[r * 256:(r + 1) * 256], codes_d[r * 256:(r + 1) * 256].cpu())
-        assert torch.equal(scales_h[r * 8:(r + 1) * 8], scales_d[r * 8:(r + 1) * 8].cpu())
-    S = cfg.n_seqs
-    ptok, pcu = synth.history_prefix_tokens(cfg)
-    tmap = up32(w.tmap)
-    cu = up32(np.arange(S + 1, dtype=np.int32))
-    tok = up32(synth.decode_tokens(cfg, 0))
-    hist = torch.empty(S * 3, dtype=torch.int32, device=DEV)
-    E.engram_history_reset(hist, p.pad_cid)
-    E.engram_history_append(hist, up32(ptok), up32(pcu), tmap, p.pad_cid)
-    idx = torch.empty(S * 24, dtype=torch.int32, device=DEV)
-    E.engram_hash(tok, cu, hist, tmap, p, idx)
-    mem_h = torch.empty(S * 6144, dtype=torch.int16, device=DEV)
-    mem_d = torch.empty_like(mem_h)
-    E.engram_gather_decode(idx, codes_h, scales_h, p.n_rows, mem_h)
-    E.engram_gather_decode(idx, codes_d, scales_d, p.n_rows, mem_d)
-    torch.cuda.synchronize()
-    assert torch.equal(mem_h, mem_d)
-    wkv = up16(synth.wkv_bf16(cfg, 1))
-    wqk = torch.from_numpy(synth.norm_weights(cfg, 1)).to(DEV)
-    outs = []
-    for codes, scales in ((codes_h, scales_h), (codes_d, scales_d)):
-        hidden = up16(synth.hidden_bf16(cfg, 1, S))
-        E.engram_forward(tok, cu, hist, tmap, p, codes, scales, wkv, wqk, hidden, cfg.H, cfg.hc)
-        torch.cuda.synchronize()
-        outs.append(down16(hidden))
-    assert np.array_equal(outs[0], outs[1])
 
 
 def test_gate_small_and_large_batch_kernels_agree_bitwise(E):
