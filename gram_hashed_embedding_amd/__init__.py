@@ -19,7 +19,7 @@ __all__ = [
     "engram_check_params", "engram_history_reset", "engram_history_fork",
     "engram_history_append", "engram_hash", "engram_gather_decode", "engram_project",
     "engram_gate", "engram_forward_workspace", "engram_precompute", "engram_gate_precomputed",
-    "engram_forward", "engram_gen_table", "engram_pack_wkv",
+    "engram_forward", "engram_forward_noalloc", "engram_gen_table", "engram_pack_wkv",
     "DEAD_TOKEN", "DEAD_IDX", "BUCKETS", "MEM", "STAGE_EVENTS", "PRECOMPUTE_STAGE_ROWS",
 ]
 
@@ -31,6 +31,7 @@ DEAD_IDX = 0xFFFFFFFF
 BUCKETS = 24
 MEM = 6144
 STAGE_EVENTS = 5
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 PRECOMPUTE_STAGE_ROWS = 0x1
 
 ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EHIP, ENGRAM_EUNSUPPORTED = 0, -1, -2, -3
@@ -102,6 +103,8 @@ def _load() -> ctypes.CDLL:
         "engram_forward": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, P, P, I32, I32, F32,
                             F32, P, SZ, P, P, P, P], ctypes.c_int),
         "engram_gen_table": ([P, P, U64, U64, U64, U64, P], ctypes.c_int),
+        "engram_forward_noalloc": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, P, P, I32, I32,
+                                    F32, F32, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -404,6 +407,37 @@ def engram_forward(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv,
         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None, _stream(stream)),
         "engram_forward")
     return ws
+
+
+def engram_forward_noalloc(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv, wqk,
+                           hidden, H: int, hc: int, eps: float = 1e-6, dot_scale: float = 1.0,
+                           gate_out=None, err_flags=None, stream=None, wkv_packed=None) -> None:
+    """engram_forward with the library's own per-GPU workspace (no
+    allocation; batches up to NOALLOC_WORKSPACE_BYTES of workspace)."""
+    torch = _torch()
+    p = HashParams.from_any(params)
+    S = cu_seqlens.numel() - 1
+    T = tok.numel()
+    if hidden.numel() != T * hc * H:
+        raise ValueError("hidden must be [T][hc][H]")
+    if wkv.numel() != (hc + 1) * H * MEM or wqk.numel() != hc * H:
+        raise ValueError("wkv must be [(hc+1)*H][6144] and wqk [hc][H]")
+    _check_packed(wkv_packed, wkv)
+    _need(hist, 3 * S, "hist")
+    _need(codes, p.n_rows * 256, "codes")
+    _need(scales, p.n_rows * 8, "scales")
+    _need(gate_out, T * hc, "gate_out")
+    _need(err_flags, 1, "err_flags")
+    _check(lib.engram_forward_noalloc(
+        _ptr(tok, _u32(torch), "tok"), _ptr(cu_seqlens, _i32(torch), "cu_seqlens"), S, T,
+        _ptr(hist, _u32(torch), "hist"), _ptr(token_map, _u32(torch), "token_map"),
+        token_map.numel(), ctypes.byref(p), _ptr(codes, torch.uint8, "codes", host_ok=True),
+        _ptr(scales, torch.uint8, "scales", host_ok=True), _ptr(wkv, _u16(torch), "wkv"),
+        _ptr(wkv_packed, _u16(torch), "wkv_packed", optional=True),
+        _ptr(wqk, torch.float32, "wqk"), _ptr(hidden, _u16(torch), "hidden"), H, hc, eps,
+        dot_scale, _ptr(gate_out, torch.float32, "gate_out", optional=True),
+        _ptr(err_flags, _u32(torch), "err_flags", optional=True), _stream(stream)),
+        "engram_forward_noalloc")
 
 
 def engram_gen_table(codes, scales, row_begin: int, n_rows: int, key_data: int, key_scale: int,

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["engram_api.cpp", "hash.hip", "gather.hip", "hash_gather.hip", "project.hip", "gate.hip",
-           "gentable.hip"]
+           "gentable.hip", "forward_noalloc.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           # keep the compiler from forming packed FP32 instructions

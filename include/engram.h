@@ -294,6 +294,26 @@ int engram_forward(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, in
                    size_t ws_bytes, float* gate_out, uint32_t* err_flags,
                    hipEvent_t* stage_events, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): engram_forward
+ * with the workspace taken from a device array of
+ * ENGRAM_NOALLOC_WORKSPACE_BYTES that the library holds on each GPU it runs
+ * on, until the process ends. Same arguments and results as engram_forward
+ * without ws, ws_bytes and stage_events. Batches whose
+ * engram_forward_workspace(T, H, hc) exceeds the array (above 1,055
+ * tokens at H = 5120, hc = 4) are rejected with ENGRAM_EINVAL before any launch. The
+ * call allocates nothing; the first call on a device looks up the array's
+ * address there. Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (two streams, two threads) race, so order them. */
+#define ENGRAM_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int engram_forward_noalloc(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                           const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                           const engram_hash_params* params, const uint8_t* codes,
+                           const uint8_t* scales, const uint16_t* wkv, const uint16_t* wkv_packed,
+                           const float* wqk, uint16_t* hidden, int32_t H, int32_t hc, float eps,
+                           float dot_scale, float* gate_out, uint32_t* err_flags,
+                           hipStream_t stream);
+
 /* ---------------------------------------------------------------- synthetic tables */
 
 /* Writes rows [row_begin, row_begin + n_rows) of a closed-form synthetic
