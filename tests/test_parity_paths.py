@@ -132,22 +132,25 @@ def _forward_every_row(E, w, H, hc, T, S, dead_spans, seed, dot_scale=1 / 16):
 
 
 @pytest.mark.parametrize("T,S,spans", [(700, 3, ((10, 5), (300, 1), (699, 1))),
+                                       (4096, 2, ((100, 576), (2000, 576), (4095, 1))),
                                        (20_000, 4, ((0, 3), (1000, 576), (9000, 576), (15000, 576),
                                                     (19990, 10)))])
 def test_forward_gate_walks_every_row(E, T, S, spans):
     """engram_forward at H = 5,120, hc = 4: at 700 tokens the gate walks
     positions (one persistent workgroup per CU, three steps each); at 20,000
     tokens with image spans it walks the packed live rows, more than 64 steps
-    per workgroup, so the kernel's per-64-step refill of the row map runs.
-    Every row's hidden and gate against the oracle's gate on the workspace's
-    k/v (which is itself checked against the oracle on sampled rows)."""
+    per workgroup, so the kernel's per-64-step refill of the row map runs; at
+    4,096 positions (rows packed, about 2,940 live) the projection's row tiles
+    past the live count stop after their first loads. Every row's hidden and
+    gate against the oracle's gate on the workspace's k/v (which is itself
+    checked against the oracle on sampled rows)."""
     log(f"forward: gate walk, T={T} S={S}, every row")
     H, hc = 5120, 4
     w = World.of("tiny")
     r = _forward_every_row(E, w, H, hc, T, S, spans, seed=T)
     dead, ws = r["dead"], r["ws"]
     n_live = int((~dead).sum())
-    if T > 1024:
+    if T > 10_000:
         assert n_live // 256 > 64        # live rows per workgroup of the walk
     ref_idx, ref_dead = _ref_idx(r["tok"], r["cu"], r["hist"], w.tmap, r["p"])
     assert np.array_equal(ref_dead, dead)
