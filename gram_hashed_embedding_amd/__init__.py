@@ -19,6 +19,7 @@ __all__ = [
     "engram_check_params", "engram_history_reset", "engram_history_fork",
     "engram_history_append", "engram_hash", "engram_gather_decode", "engram_project",
     "engram_gate", "engram_forward_workspace", "engram_precompute", "engram_gate_precomputed",
+    "engram_precompute_buckets", "BucketTable",
     "engram_forward", "engram_forward_noalloc", "engram_gen_table", "engram_pack_wkv",
     "DEAD_TOKEN", "DEAD_IDX", "BUCKETS", "MEM", "STAGE_EVENTS", "PRECOMPUTE_STAGE_ROWS",
 ]
@@ -41,6 +42,11 @@ class EngramError(RuntimeError):
     def __init__(self, status: int, fn: str, detail: str):
         super().__init__(f"{fn}: {_status(status)}: {detail}")
         self.status = status
+
+
+class BucketTable(ctypes.Structure):
+    """Mirror of engram_bucket_table (a table held as one allocation per bucket)."""
+    _fields_ = [("codes", ctypes.c_void_p * 24), ("scales", ctypes.c_void_p * 24)]
 
 
 class HashParams(ctypes.Structure):
@@ -100,6 +106,8 @@ def _load() -> ctypes.CDLL:
                                P, P], ctypes.c_int),
         "engram_gate_precomputed": ([P, P, SZ, P, I32, I64, P, I32, I32, F32, F32, P, P],
                                     ctypes.c_int),
+        "engram_precompute_buckets": ([P, P, I32, I64, P, P, U32, P, P, P, P, I32, I32, U32, P,
+                                       SZ, P, P], ctypes.c_int),
         "engram_forward": ([P, P, I32, I64, P, P, U32, P, P, P, P, P, P, P, I32, I32, F32,
                             F32, P, SZ, P, P, P, P], ctypes.c_int),
         "engram_gen_table": ([P, P, U64, U64, U64, U64, P], ctypes.c_int),
@@ -344,6 +352,54 @@ def engram_precompute(tok, cu_seqlens, hist, token_map, params, codes, scales, w
     return ws
 
 
+def _table_ptr(x, name, nbytes):
+    """A bucket's address: a device or pinned host tensor (of at least nbytes),
+    or an int (the address of nbytes of device memory or of pinned host memory
+    mapped at its host address, e.g. from hipHostMalloc)."""
+    torch = _torch()
+    if isinstance(x, int):
+        if x == 0:
+            raise ValueError(f"{name} is NULL")
+        return x
+    _need(x, nbytes, name)
+    return _ptr(x, torch.uint8, name, host_ok=True)
+
+
+def engram_precompute_buckets(tok, cu_seqlens, hist, token_map, params, codes, scales, wkv,
+                              H: int, hc: int, ws=None, flags: int = 0, err_flags=None,
+                              stream=None, wkv_packed=None):
+    """engram_precompute with the table given per bucket: codes[j] / scales[j]
+    hold bucket j's prime[j] rows (24 of each). Returns the workspace."""
+    torch = _torch()
+    p = HashParams.from_any(params)
+    if len(codes) != BUCKETS or len(scales) != BUCKETS:
+        raise ValueError("codes and scales must list 24 buckets each")
+    tbl = BucketTable()
+    for j in range(BUCKETS):
+        tbl.codes[j] = _table_ptr(codes[j], f"codes[{j}]", int(p.prime[j]) * 256)
+        tbl.scales[j] = _table_ptr(scales[j], f"scales[{j}]", int(p.prime[j]) * 8)
+    S = cu_seqlens.numel() - 1
+    T = tok.numel()
+    if wkv.numel() != (hc + 1) * H * MEM:
+        raise ValueError("wkv must be [(hc+1)*H][6144]")
+    _check_packed(wkv_packed, wkv)
+    _need(hist, 3 * S, "hist")
+    _need(err_flags, 1, "err_flags")
+    need = engram_forward_workspace(T, H, hc)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=wkv.device)
+    _need(ws, need, "ws")
+    _check(lib.engram_precompute_buckets(
+        _ptr(tok, _u32(torch), "tok"), _ptr(cu_seqlens, _i32(torch), "cu_seqlens"), S, T,
+        _ptr(hist, _u32(torch), "hist"), _ptr(token_map, _u32(torch), "token_map"),
+        token_map.numel(), ctypes.byref(p), ctypes.byref(tbl), _ptr(wkv, _u16(torch), "wkv"),
+        _ptr(wkv_packed, _u16(torch), "wkv_packed", optional=True), H, hc, flags,
+        _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _ptr(err_flags, _u32(torch), "err_flags", optional=True), _stream(stream)),
+        "engram_precompute_buckets")
+    return ws
+
+
 def engram_gate_precomputed(hidden, ws, tok, S: int, wqk, H: int, hc: int, eps: float = 1e-6,
                             dot_scale: float = 1.0, gate_out=None, stream=None) -> None:
     """The gate at layer entry, reading the k/v engram_precompute left in ws
@@ -442,9 +498,9 @@ def engram_forward_noalloc(tok, cu_seqlens, hist, token_map, params, codes, scal
 
 def engram_gen_table(codes, scales, row_begin: int, n_rows: int, key_data: int, key_scale: int,
                      stream=None) -> None:
-    torch = _torch()
-    if codes.numel() < n_rows * 256 or scales.numel() < n_rows * 8:
-        raise ValueError("codes/scales too small for n_rows")
-    _check(lib.engram_gen_table(_ptr(codes, torch.uint8, "codes", host_ok=True), _ptr(scales, torch.uint8, "scales", host_ok=True),
+    """codes/scales: tensors (device or pinned host) or int addresses (see
+    engram_precompute_buckets) of at least n_rows rows."""
+    _check(lib.engram_gen_table(_table_ptr(codes, "codes", n_rows * 256),
+                                _table_ptr(scales, "scales", n_rows * 8),
                                 row_begin, n_rows, key_data, key_scale, _stream(stream)),
            "engram_gen_table")

@@ -51,4 +51,45 @@ __device__ __forceinline__ void decode_store_row(uint16_t* out, int l, bool live
   nt_store16(out + 128 + l * 8, b.x, b.y, b.z, b.w);
 }
 
+// Rows of a table kept as one allocation per bucket (TableBuckets): a
+// workgroup copies the 24 bases and row ranges into LDS once; a lane group
+// then finds row `row` of bucket j at codes[j] + (row - first[j]) * 256.
+struct BucketLds {
+  uint64_t codes[ENGRAM_BUCKETS];
+  uint64_t scales[ENGRAM_BUCKETS];
+  uint32_t first[ENGRAM_BUCKETS];
+  uint32_t count[ENGRAM_BUCKETS];
+};
+
+__device__ __forceinline__ void load_buckets(const TableBuckets& tb, BucketLds& b) {
+  const int i = threadIdx.x;
+  if (i < ENGRAM_BUCKETS) {
+    b.codes[i] = tb.codes[i];
+    b.scales[i] = tb.scales[i];
+    b.first[i] = tb.first[i];
+    b.count[i] = tb.count[i];
+  }
+  __syncthreads();
+}
+
+// Code and scale addresses of table row `row` for bucket j, and whether the
+// row is in the table (for a bucketed table: in bucket j's range).
+template <bool BK>
+__device__ __forceinline__ bool row_address(const uint8_t* codes, const uint8_t* scales,
+                                            uint64_t n_rows, const BucketLds* b, int j,
+                                            uint32_t row, const uint8_t*& cr, const uint8_t*& sr) {
+  if constexpr (BK) {
+    const uint32_t k = row - b->first[j];
+    if (k >= b->count[j]) return false;
+    cr = reinterpret_cast<const uint8_t*>(b->codes[j]) + (uint64_t)k * ENGRAM_ROW;
+    sr = reinterpret_cast<const uint8_t*>(b->scales[j]) + (uint64_t)k * ENGRAM_SCALES_PER_ROW;
+    return true;
+  } else {
+    if ((uint64_t)row >= n_rows) return false;
+    cr = codes + (uint64_t)row * ENGRAM_ROW;
+    sr = scales + (uint64_t)row * ENGRAM_SCALES_PER_ROW;
+    return true;
+  }
+}
+
 }  // namespace engram

@@ -211,7 +211,7 @@ int enqueue_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S
                        const engram_hash_params& params, const uint8_t* codes, const uint8_t* scales,
                        const uint16_t* wkv, const uint16_t* wkv_packed, int32_t H, int32_t hc,
                        uint32_t flags, void* ws, uint32_t* err_flags, hipEvent_t* ev,
-                       hipStream_t stream) {
+                       hipStream_t stream, const engram::TableBuckets* tb = nullptr) {
   int rc;
   auto mark = [&](int i) -> int {
     if (ev == nullptr) return ENGRAM_OK;
@@ -226,7 +226,7 @@ int enqueue_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S
     // Small batch: one kernel hashes, gathers and decodes; events 1 and 2
     // both mark its end.
     rc = from_hip(engram::launch_hash_gather(tok, cu_seqlens, S, T, hist, token_map, map_len, params,
-                                             codes, scales, w.idx, w.mem, err_flags, stream),
+                                             codes, scales, w.idx, w.mem, err_flags, stream, tb),
                   "engram_precompute: hash + gather");
     if (rc != ENGRAM_OK) return rc;
     if ((rc = mark(1)) != ENGRAM_OK) return rc;
@@ -248,13 +248,13 @@ int enqueue_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S
     if ((rc = mark(1)) != ENGRAM_OK) return rc;
     if (stage) {
       rc = from_hip(engram::launch_stage_rows(w.idx, T, codes, scales, params.n_rows, w.stage_codes,
-                                              w.stage_scales, err_flags, stream),
+                                              w.stage_scales, err_flags, stream, tb),
                     "engram_precompute: stage rows");
       if (rc != ENGRAM_OK) return rc;
     }
     rc = from_hip(engram::launch_gather_decode(w.idx, T, stage ? w.stage_codes : codes,
                                                stage ? w.stage_scales : scales, params.n_rows, w.mem,
-                                               slot, stage, err_flags, stream),
+                                               slot, stage, err_flags, stream, tb),
                   "engram_precompute: gather + decode");
     if (rc != ENGRAM_OK) return rc;
   } else if ((rc = mark(1)) != ENGRAM_OK) {
@@ -454,6 +454,35 @@ int engram_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S,
   if (rc != ENGRAM_OK) return rc;
   return enqueue_precompute(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, codes, scales,
                             wkv, wkv_packed, H, hc, flags, ws, err_flags, nullptr, stream);
+}
+
+int engram_precompute_buckets(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                              const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                              const engram_hash_params* params, const engram_bucket_table* table,
+                              const uint16_t* wkv, const uint16_t* wkv_packed, int32_t H, int32_t hc,
+                              uint32_t flags, void* ws, size_t ws_bytes, uint32_t* err_flags,
+                              hipStream_t stream) {
+  if (table == nullptr) return fail(ENGRAM_EINVAL, "table is NULL");
+  engram::TableBuckets tb;
+  for (int j = 0; j < ENGRAM_BUCKETS; ++j) {
+    if (T > 0 && (table->codes[j] == nullptr || table->scales[j] == nullptr))
+      return fail(ENGRAM_EINVAL, "bucket %d: codes or scales is NULL", j);
+    if (!aligned(table->codes[j], 16) || !aligned(table->scales[j], 8))
+      return fail(ENGRAM_EINVAL, "bucket %d: codes 16-byte and scales 8-byte alignment required", j);
+    tb.codes[j] = reinterpret_cast<uint64_t>(table->codes[j]);
+    tb.scales[j] = reinterpret_cast<uint64_t>(table->scales[j]);
+  }
+  // the gather's own checks see bucket 0's pointers as the table
+  const int rc = check_precompute_args(tok, cu_seqlens, S, T, hist, token_map, map_len, params,
+                                       table->codes[0], table->scales[0], wkv, wkv_packed, H, hc,
+                                       flags, ws, ws_bytes);
+  if (rc != ENGRAM_OK) return rc;
+  for (int j = 0; j < ENGRAM_BUCKETS; ++j) {
+    tb.first[j] = (uint32_t)params->offset[j];
+    tb.count[j] = params->prime[j];
+  }
+  return enqueue_precompute(tok, cu_seqlens, S, T, hist, token_map, map_len, *params, nullptr, nullptr,
+                            wkv, wkv_packed, H, hc, flags, ws, err_flags, nullptr, stream, &tb);
 }
 
 int engram_gate_precomputed(uint16_t* hidden, const void* ws, size_t ws_bytes, const uint32_t* tok,

@@ -30,21 +30,34 @@ constexpr int64_t kLiveChunkPositions = 4096;
 inline int64_t live_chunks(int64_t T) { return (T + kLiveChunkPositions - 1) / kLiveChunkPositions; }
 hipError_t launch_live_slots(const uint32_t* tok, int64_t T, uint32_t* slot, uint32_t* count,
                              uint32_t* chunk_count, uint32_t* live_pos, hipStream_t st);
+// A table kept as one allocation per bucket: bucket j's rows first[j] ..
+// first[j] + count[j] - 1 start at codes[j] / scales[j] (device addresses).
+struct TableBuckets {
+  uint64_t codes[ENGRAM_BUCKETS];
+  uint64_t scales[ENGRAM_BUCKETS];
+  uint32_t first[ENGRAM_BUCKETS];
+  uint32_t count[ENGRAM_BUCKETS];
+};
+
 // slot: NULL (position t's rows go to mem row t), or the live_slots map
 // (they go to row slot[t]; DEAD positions write nothing).
 // staged: codes/scales are launch_stage_rows' staging area, where row
 // t*24 + j holds table row idx[t][j] (idx still marks DEAD and out-of-range
 // rows); otherwise they are the table and row idx[t][j] is read.
+// tb: NULL (codes/scales hold the table), or the table's buckets (codes and
+// scales then only matter with `staged`).
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                                 const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
-                                const uint32_t* slot, bool staged, uint32_t* err, hipStream_t st);
+                                const uint32_t* slot, bool staged, uint32_t* err, hipStream_t st,
+                                const TableBuckets* tb = nullptr);
 // Copies table row idx[t][j] (256 code bytes, 8 scale bytes) to row t*24 + j
 // of a staging area in device memory, for tables in pinned host memory:
 // every row crosses the host link once, in 16-byte loads with many rows in
 // flight. DEAD and out-of-range rows are skipped (the latter flagged).
 hipError_t launch_stage_rows(const uint32_t* idx, int64_t T, const uint8_t* codes,
                              const uint8_t* scales, uint64_t n_rows, uint8_t* stage_codes,
-                             uint8_t* stage_scales, uint32_t* err, hipStream_t st);
+                             uint8_t* stage_scales, uint32_t* err, hipStream_t st,
+                             const TableBuckets* tb = nullptr);
 // Hash, gather and decode as one kernel (hash_gather.hip): for batches of at
 // most kHashGatherMaxTokens tokens in at most kHashGatherMaxSeqs sequences,
 // where both steps are latency-bound chains of loads. Writes the same idx and
@@ -55,7 +68,7 @@ hipError_t launch_hash_gather(const uint32_t* tok, const int32_t* cu, int32_t S,
                               const uint32_t* hist, const uint32_t* map, uint32_t map_len,
                               const engram_hash_params& p, const uint8_t* codes,
                               const uint8_t* scales, uint32_t* idx, uint16_t* mem, uint32_t* err,
-                              hipStream_t st);
+                              hipStream_t st, const TableBuckets* tb = nullptr);
 // live_rows: NULL, or a device word holding how many of the T rows of mem
 // count (T > 256 only; rows past it are neither computed in full nor stored).
 // wkv_packed: NULL, or wkv in the packed decode layout (launch_pack_wkv),

@@ -25,11 +25,15 @@ constexpr int kGroups = kBlock / 16;     // rows per pass of one workgroup
 constexpr int kRowsInFlight = 4;         // passes per workgroup (rows per lane)
 
 // With `slot` (from live_slots_kernel), position t's rows go to row slot[t]
-// of mem and a DEAD position writes nothing; without it, to row t.
+// of mem and a DEAD position writes nothing; without it, to row t. BK: the
+// table is one allocation per bucket (tb), not codes/scales.
+template <bool BK>
 __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
     const uint32_t* __restrict__ idx, int64_t total_rows, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, uint64_t n_rows, uint16_t* __restrict__ mem,
-    const uint32_t* __restrict__ slot, bool staged, uint32_t* err) {
+    const uint32_t* __restrict__ slot, bool staged, uint32_t* err, const TableBuckets tb) {
+  __shared__ BucketLds bl;
+  if constexpr (BK) load_buckets(tb, bl);
   const int l = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;
   const int64_t base = (int64_t)blockIdx.x * (kGroups * kRowsInFlight);
@@ -58,13 +62,18 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
       }
       const uint32_t row = idx[r];
       if (row != ENGRAM_DEAD_IDX) {
-        if ((uint64_t)row < n_rows) {
+        const uint8_t *cr = nullptr, *sr = nullptr;
+        const bool in_table = row_address<BK>(codes, scales, n_rows, &bl,
+                                                       (int)(r % ENGRAM_BUCKETS), row, cr, sr);
+        if (in_table) {
           live[u] = true;
-          const uint64_t src = staged ? (uint64_t)r : (uint64_t)row;
-          const uint8_t* cr = codes + src * ENGRAM_ROW;
+          if (staged) {   // the row was copied to staging row r
+            cr = codes + (uint64_t)r * ENGRAM_ROW;
+            sr = scales + (uint64_t)r * ENGRAM_SCALES_PER_ROW;
+          }
           ca[u] = *reinterpret_cast<const uint2*>(cr + l * 8);
           cb[u] = *reinterpret_cast<const uint2*>(cr + 128 + l * 8);
-          const uint2 s2 = *reinterpret_cast<const uint2*>(scales + src * ENGRAM_SCALES_PER_ROW);
+          const uint2 s2 = *reinterpret_cast<const uint2*>(sr);
           sa[u] = (s2.x >> sh) & 0xFFu;
           sb[u] = (s2.y >> sh) & 0xFFu;
         } else {
@@ -86,10 +95,13 @@ __global__ __launch_bounds__(kBlock) void gather_decode_kernel(
 // read crosses the host link and waits on its latency.
 constexpr int kStageRowsInFlight = 8;
 
+template <bool BK>
 __global__ __launch_bounds__(kBlock) void stage_rows_kernel(
     const uint32_t* __restrict__ idx, int64_t total_rows, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, uint64_t n_rows, uint8_t* __restrict__ stage_codes,
-    uint8_t* __restrict__ stage_scales, uint32_t* err) {
+    uint8_t* __restrict__ stage_scales, uint32_t* err, const TableBuckets tb) {
+  __shared__ BucketLds bl;
+  if constexpr (BK) load_buckets(tb, bl);
   const int l = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;
   const int64_t base = (int64_t)blockIdx.x * (kGroups * kStageRowsInFlight);
@@ -105,11 +117,11 @@ __global__ __launch_bounds__(kBlock) void stage_rows_kernel(
     if (r < total_rows) {
       const uint32_t row = idx[r];
       if (row != ENGRAM_DEAD_IDX) {
-        if ((uint64_t)row < n_rows) {
+        const uint8_t *cr = nullptr, *sr = nullptr;
+        if (row_address<BK>(codes, scales, n_rows, &bl, (int)(r % ENGRAM_BUCKETS), row, cr, sr)) {
           go[u] = true;
-          c[u] = *reinterpret_cast<const uint4*>(codes + (uint64_t)row * ENGRAM_ROW + l * 16);
-          if (l == 0)
-            sc[u] = *reinterpret_cast<const uint2*>(scales + (uint64_t)row * ENGRAM_SCALES_PER_ROW);
+          c[u] = *reinterpret_cast<const uint4*>(cr + l * 16);
+          if (l == 0) sc[u] = *reinterpret_cast<const uint2*>(sr);
         } else {
           set_err(err, ENGRAM_ERR_ROW_RANGE);
         }
@@ -129,25 +141,35 @@ __global__ __launch_bounds__(kBlock) void stage_rows_kernel(
 
 hipError_t launch_stage_rows(const uint32_t* idx, int64_t T, const uint8_t* codes,
                              const uint8_t* scales, uint64_t n_rows, uint8_t* stage_codes,
-                             uint8_t* stage_scales, uint32_t* err, hipStream_t st) {
+                             uint8_t* stage_scales, uint32_t* err, hipStream_t st,
+                             const TableBuckets* tb) {
   const int64_t rows = T * ENGRAM_BUCKETS;
   if (rows == 0) return hipSuccess;
   const int64_t per_block = (int64_t)kGroups * kStageRowsInFlight;
   const unsigned blocks = (unsigned)((rows + per_block - 1) / per_block);
-  stage_rows_kernel<<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, stage_codes,
-                                               stage_scales, err);
+  if (tb != nullptr)
+    stage_rows_kernel<true><<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, stage_codes,
+                                                       stage_scales, err, *tb);
+  else
+    stage_rows_kernel<false><<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows,
+                                                        stage_codes, stage_scales, err, TableBuckets{});
   return hipGetLastError();
 }
 
 hipError_t launch_gather_decode(const uint32_t* idx, int64_t T, const uint8_t* codes,
                                 const uint8_t* scales, uint64_t n_rows, uint16_t* mem,
-                                const uint32_t* slot, bool staged, uint32_t* err, hipStream_t st) {
+                                const uint32_t* slot, bool staged, uint32_t* err, hipStream_t st,
+                                const TableBuckets* tb) {
   const int64_t rows = T * ENGRAM_BUCKETS;
   if (rows == 0) return hipSuccess;
   const int64_t per_block = (int64_t)kGroups * kRowsInFlight;
   const unsigned blocks = (unsigned)((rows + per_block - 1) / per_block);
-  gather_decode_kernel<<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, mem, slot, staged,
-                                                  err);
+  if (tb != nullptr && !staged)
+    gather_decode_kernel<true><<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, mem, slot,
+                                                          false, err, *tb);
+  else
+    gather_decode_kernel<false><<<blocks, kBlock, 0, st>>>(idx, rows, codes, scales, n_rows, mem, slot,
+                                                           staged, err, TableBuckets{});
   return hipGetLastError();
 }
 

@@ -24,15 +24,17 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kGroups = kBlock / 16;   // rows per pass of one workgroup
 
-template <int RIF>
+template <int RIF, bool BK>
 __global__ __launch_bounds__(kBlock) void hash_gather_kernel(
     const uint32_t* __restrict__ tok, const int32_t* __restrict__ cu, int32_t S, int64_t T,
     const uint32_t* __restrict__ hist, const uint32_t* __restrict__ map, uint32_t map_len,
     const engram_hash_params p, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, uint32_t* __restrict__ idx, uint16_t* __restrict__ mem,
-    uint32_t* err) {
+    uint32_t* err, const TableBuckets tb) {
   __shared__ int32_t cu_s[kHashGatherMaxSeqs + 1];
+  __shared__ BucketLds bl;
   for (int i = threadIdx.x; i <= S; i += kBlock) cu_s[i] = cu[i];
+  if constexpr (BK) load_buckets(tb, bl);   // (its barrier also publishes cu_s)
   __syncthreads();
 
   const int l = threadIdx.x & 15;
@@ -58,12 +60,12 @@ __global__ __launch_bounds__(kBlock) void hash_gather_kernel(
                                : bucket_row(tok, cu_s, S, T, hist, map, map_len, p, t, j, tk, err);
       if (l == 0) idx[r] = row;
       if (row != ENGRAM_DEAD_IDX) {
-        if ((uint64_t)row < p.n_rows) {
+        const uint8_t *cr = nullptr, *sr = nullptr;
+        if (row_address<BK>(codes, scales, p.n_rows, &bl, j, row, cr, sr)) {
           live[u] = true;
-          const uint8_t* cr = codes + (uint64_t)row * ENGRAM_ROW;
           ca[u] = *reinterpret_cast<const uint2*>(cr + l * 8);
           cb[u] = *reinterpret_cast<const uint2*>(cr + 128 + l * 8);
-          const uint2 s2 = *reinterpret_cast<const uint2*>(scales + (uint64_t)row * ENGRAM_SCALES_PER_ROW);
+          const uint2 s2 = *reinterpret_cast<const uint2*>(sr);
           sa[u] = (s2.x >> sh) & 0xFFu;
           sb[u] = (s2.y >> sh) & 0xFFu;
         } else {
@@ -86,14 +88,19 @@ hipError_t launch_hash_gather(const uint32_t* tok, const int32_t* cu, int32_t S,
                               const uint32_t* hist, const uint32_t* map, uint32_t map_len,
                               const engram_hash_params& p, const uint8_t* codes,
                               const uint8_t* scales, uint32_t* idx, uint16_t* mem, uint32_t* err,
-                              hipStream_t st) {
+                              hipStream_t st, const TableBuckets* tb) {
   if (T == 0) return hipSuccess;
   if (T > kHashGatherMaxTokens || S < 1 || S > kHashGatherMaxSeqs) return hipErrorInvalidValue;
   constexpr int kRif = 1;
   const int64_t rows = T * ENGRAM_BUCKETS;
   const unsigned blocks = (unsigned)((rows + kGroups * kRif - 1) / (kGroups * kRif));
-  hash_gather_kernel<kRif><<<blocks, kBlock, 0, st>>>(tok, cu, S, T, hist, map, map_len, p, codes,
-                                                      scales, idx, mem, err);
+  if (tb != nullptr)
+    hash_gather_kernel<kRif, true><<<blocks, kBlock, 0, st>>>(tok, cu, S, T, hist, map, map_len, p,
+                                                              codes, scales, idx, mem, err, *tb);
+  else
+    hash_gather_kernel<kRif, false><<<blocks, kBlock, 0, st>>>(tok, cu, S, T, hist, map, map_len, p,
+                                                               codes, scales, idx, mem, err,
+                                                               TableBuckets{});
   return hipGetLastError();
 }
 

@@ -251,6 +251,29 @@ int engram_precompute(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S,
                       uint32_t flags, void* ws, size_t ws_bytes, uint32_t* err_flags,
                       hipStream_t stream);
 
+/* A layer's table kept as one allocation per bucket: bucket j's rows
+ * offset[j] .. offset[j] + prime[j] - 1 (engram_hash_params) are the
+ * uint8[prime[j]][256] codes at codes[j] and the uint8[prime[j]][8] scales at
+ * scales[j] (16- and 8-byte aligned; device memory or pinned host memory
+ * mapped at its host address, as for the one-allocation table). For tables
+ * in pinned host memory, where one allocation of a full-size table (98.3 GB
+ * of codes) may be refused ([vLLM] CPU offload: tables stay in host
+ * memory and HBM holds the KV cache instead). */
+typedef struct {
+  const uint8_t* codes[ENGRAM_BUCKETS];
+  const uint8_t* scales[ENGRAM_BUCKETS];
+} engram_bucket_table;
+
+/* engram_precompute with the table given per bucket (engram_bucket_table):
+ * the same work, results and checks; a row is read from its bucket's
+ * allocation. */
+int engram_precompute_buckets(const uint32_t* tok, const int32_t* cu_seqlens, int32_t S, int64_t T,
+                              const uint32_t* hist, const uint32_t* token_map, uint32_t map_len,
+                              const engram_hash_params* params, const engram_bucket_table* table,
+                              const uint16_t* wkv, const uint16_t* wkv_packed, int32_t H, int32_t hc,
+                              uint32_t flags, void* ws, size_t ws_bytes, uint32_t* err_flags,
+                              hipStream_t stream);
+
 /* The gate at layer entry ([zLLM] 提前投影: only the gate reads the layer's
  * hidden state): engram_gate on hidden[T][hc][H] with the keys and value
  * that engram_precompute left in `ws` for the same tok, S, T, H and hc

@@ -31,7 +31,8 @@ def test_header_declares_the_stage_entry_points():
     for n in ("engram_hash", "engram_gather_decode", "engram_project", "engram_gate",
               "engram_forward", "engram_history_append", "engram_history_fork",
               "engram_history_reset", "engram_check_params", "engram_forward_workspace",
-              "engram_pack_wkv", "engram_precompute", "engram_gate_precomputed"):
+              "engram_pack_wkv", "engram_precompute", "engram_gate_precomputed",
+              "engram_precompute_buckets"):
         assert n in names
 
 
@@ -202,6 +203,37 @@ def test_precompute_and_gate_precomputed_check_arguments_before_launch(E):
                                None, H, hc, 0, None, 0, None, None) == 0
     assert L.engram_gate_precomputed(None, None, 0, None, 1, 0, None, H, hc, 1e-6, 1.0, None,
                                      None) == 0
+
+
+def test_precompute_buckets_checks_the_bucket_table_before_launch(E):
+    """engram_precompute_buckets rejects a missing table, a NULL or misaligned
+    bucket pointer and the precompute's own bad arguments before any launch."""
+    L = E.lib
+    p, _ = _params()
+    hp = E.HashParams.from_any(p)
+    fake = ctypes.c_void_p(0x10000)
+    H, hc, T = 256, 4, 8
+    need = L.engram_forward_workspace(T, H, hc)
+    ws = ctypes.c_void_p(0x100000)
+
+    def call(tbl, hp=hp):
+        return L.engram_precompute_buckets(fake, fake, 1, T, fake, fake, 10, ctypes.byref(hp),
+                                           None if tbl is None else ctypes.byref(tbl), fake, None,
+                                           H, hc, 0, ws, need, None, None)
+    good = E.BucketTable()
+    for j in range(24):
+        good.codes[j] = 0x1000000 + j * 0x10000
+        good.scales[j] = 0x2000000 + j * 0x1000
+    assert call(None) == -1 and b"table" in L.engram_last_error()
+    t = E.BucketTable.from_buffer_copy(good)
+    t.codes[5] = None
+    assert call(t) == -1 and b"bucket 5" in L.engram_last_error()
+    t = E.BucketTable.from_buffer_copy(good)
+    t.scales[23] = 0x2000004
+    assert call(t) == -1 and b"bucket 23" in L.engram_last_error()
+    bad = E.HashParams.from_any(p)
+    bad.prime[0] = 4
+    assert call(good, bad) == -1
 
 
 def test_pack_wkv_rejects_bad_arguments_before_launch(E):

@@ -362,3 +362,77 @@ def test_host_table_precompute_in_place_and_staged_against_oracle(E):
             got_kv[~has] = 0
             check_gate_rows(down16(h).reshape(T, hc, H)[rows], g.cpu().numpy().reshape(T, hc)[rows],
                         hidden[rows], got_kv, ref_kv, wqk, dead[rows], H, hc, 1.0, name)
+
+
+# ---------------------------------------------------------------- per-bucket tables (f3)
+def _bucket_table(E, p, keys, pinned):
+    """The layer's table as 24 allocations, bucket j holding rows offset[j] ..
+    offset[j] + prime[j] - 1, written by the same closed-form generator."""
+    codes, scales = [], []
+    for j in range(24):
+        n = int(p.prime[j])
+        if pinned:
+            c = torch.empty(n * 256, dtype=torch.uint8, pin_memory=True)
+            s = torch.empty(n * 8, dtype=torch.uint8, pin_memory=True)
+        else:
+            c = torch.empty(n * 256, dtype=torch.uint8, device=DEV)
+            s = torch.empty(n * 8, dtype=torch.uint8, device=DEV)
+        E.engram_gen_table(c, s, int(p.offset[j]), n, *keys)
+        codes.append(c)
+        scales.append(s)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+@pytest.mark.parametrize("where", ["device", "pinned host"])
+def test_bucket_table_precompute_against_oracle(E, where):
+    """The decode config's table held as 24 allocations (device memory, or
+    pinned host memory mapped into the device's address space) through
+    engram_precompute_buckets, read in place and staged: a decode step (the
+    fused hash + gather kernel) and a 2,000-token packed batch. Indices and
+    decoded rows bit-exact against the oracle and bit-identical (with k/v) to
+    the one-allocation table; hidden states and gates against the oracle."""
+    log(f"bucket table ({where}): decode step and 2,000-token batch, in place and staged")
+    w = World.of("decode")
+    cfg, p = w.cfg, w.params[0]
+    bc, bs = _bucket_table(E, p, w.keys[0], pinned=where != "device")
+    codes, scales = device_table(E, p.n_rows, *w.keys[0])
+    H, hc = cfg.H, cfg.hc
+    wkv = synth.wkv_bf16(cfg, 1)
+    wqk = synth.norm_weights(cfg, 1)
+    wkv_d, wqk_d, tmap = up16(wkv), upf(wqk), up32(w.tmap)
+    rng = np.random.default_rng(17)
+    cases = [(synth.decode_tokens(cfg, 1), np.arange(cfg.n_seqs + 1, dtype=np.int32),
+              rng.integers(0, cfg.vocab_c, (cfg.n_seqs, 3)).astype(np.uint32))]
+    cases.append(_ragged(rng, 4, 2000, cfg.map_len, cfg.vocab_c))
+    for tok, cu, hist in cases:
+        T, S = len(tok), len(cu) - 1
+        args = (up32(tok), up32(cu), up32(hist), tmap, p)
+        ref_idx, dead = _ref_idx(tok, cu, hist, w.tmap, p)
+        rows = np.unique(np.concatenate([rng.integers(0, T, min(T, 40)), np.flatnonzero(dead)[:3]]))
+        ref_mem = O.gather_decode(ref_idx[rows], w.rows(0))
+        ref_kv = O.project(ref_mem, wkv)
+        hidden = synth.hidden_bf16(cfg, 1, T, batch=3)
+        ws_one = E.engram_precompute(*args, codes, scales, wkv_d, H, hc)
+        for flags in (0, E.PRECOMPUTE_STAGE_ROWS):
+            err = torch.zeros(1, dtype=torch.int32, device=DEV)
+            ws = E.engram_precompute_buckets(*args, bc, bs, wkv_d, H, hc, flags=flags, err_flags=err)
+            h = up16(hidden)
+            g = torch.empty(T * hc, dtype=torch.float32, device=DEV)
+            E.engram_gate_precomputed(h, ws, up32(tok), S, wqk_d, H, hc, gate_out=g)
+            torch.cuda.synchronize()
+            assert int(err.item()) == 0
+            v_one, v_b = workspace_views(ws_one, T, H, hc), workspace_views(ws, T, H, hc)
+            assert np.array_equal(down32(v_b[0]).reshape(T, 24), ref_idx)
+            # rows in use: all T, or (packed) the live rows only, the rest unwritten
+            n = T if T <= 1024 else int((~dead).sum())
+            assert torch.equal(v_one[2][:n * 6144], v_b[2][:n * 6144])                  # mem
+            assert torch.equal(v_one[3][:n * (hc + 1) * H], v_b[3][:n * (hc + 1) * H])  # k/v
+            if T > 1024:
+                assert torch.equal(v_one[1], v_b[1])                                    # slot
+            got_mem, got_kv, has = forward_rows(ws, T, S, H, hc, rows)
+            assert np.array_equal(got_mem[has], ref_mem[has])
+            assert_bf16_close(got_kv[has], ref_kv[has], what="kv")
+            got_kv[~has] = 0
+            check_gate_rows(down16(h).reshape(T, hc, H)[rows], g.cpu().numpy().reshape(T, hc)[rows],
+                            hidden[rows], got_kv, ref_kv, wqk, dead[rows], H, hc, 1.0, f"T={T} flags={flags}")
