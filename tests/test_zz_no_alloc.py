@@ -1,7 +1,8 @@
 """engram_forward_noalloc (the entry point that allocates nothing) against
-engram_forward and the oracle, through the C ABI, on two calls in a row:
-the second with a smaller batch, so it runs on the device array the first
-call left behind."""
+engram_forward and the oracle, through the C ABI, on calls in a row that
+each run on the device array the previous call left behind: a batch that
+packs its live rows (above 1,024 tokens), a smaller one that does not, one
+that packs because it has more than 1,024 sequences, and a decode-sized one."""
 import numpy as np
 import pytest
 import torch
@@ -9,8 +10,8 @@ import torch
 import engram_synth as synth
 from oracle import engram_oracle as O
 from tests.conftest import gpu_available
-from tests.gpu_helpers import (DEV, World, assert_bf16_close, device_table, down16, log, up16,
-                               up32, upf)
+from tests.gpu_helpers import (DEV, World, assert_bf16_close, check_gate_rows, device_table, down16,
+                               forward_rows, log, up16, up32, upf)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X")]
@@ -26,7 +27,7 @@ def _batch(rng, S, T, map_len, vocab_c):
     return tok, cu, hist
 
 
-def test_forward_noalloc_matches_forward_twice_then_rejects_oversize():
+def test_forward_noalloc_matches_forward_on_calls_in_a_row_then_rejects_oversize():
     import gram_hashed_embedding_amd as E
     w = World.of("decode")
     cfg, p = w.cfg, w.params[0]
@@ -36,7 +37,8 @@ def test_forward_noalloc_matches_forward_twice_then_rejects_oversize():
     wqk = synth.norm_weights(cfg, 1)
     wkv_d, wqk_d, tmap_d = up16(wkv), upf(wqk), up32(w.tmap)
     rng = np.random.default_rng(77)
-    for call, (S, T, dot_scale) in enumerate(((37, 1000, 1 / 16), (64, 64, 1.0))):
+    for call, (S, T, dot_scale) in enumerate(((3, 1050, 1 / 16), (37, 1000, 1 / 16),
+                                              (1030, 1040, 1 / 16), (64, 64, 1.0))):
         log(f"noalloc call {call}: S={S} T={T} dot_scale={dot_scale}")
         tok, cu, hist = _batch(rng, S, T, cfg.map_len, p.vocab_c)
         hidden = synth.hidden_bf16(cfg, 1, T, batch=call)
@@ -46,7 +48,9 @@ def test_forward_noalloc_matches_forward_twice_then_rejects_oversize():
         g_na = torch.full((T * cfg.hc,), -1.0, dtype=torch.float32, device=DEV)
         e_ref = torch.zeros(1, dtype=torch.int32, device=DEV)
         e_na = torch.zeros(1, dtype=torch.int32, device=DEV)
-        E.engram_forward(*args, h_ref, cfg.H, cfg.hc, 1e-6, dot_scale, gate_out=g_ref, err_flags=e_ref)
+        ws = torch.empty(E.engram_forward_workspace(T, cfg.H, cfg.hc), dtype=torch.uint8, device=DEV)
+        E.engram_forward(*args, h_ref, cfg.H, cfg.hc, 1e-6, dot_scale, ws=ws, gate_out=g_ref,
+                         err_flags=e_ref)
         E.engram_forward_noalloc(*args, h_na, cfg.H, cfg.hc, 1e-6, dot_scale, gate_out=g_na,
                                  err_flags=e_na)
         torch.cuda.synchronize()
@@ -54,21 +58,22 @@ def test_forward_noalloc_matches_forward_twice_then_rejects_oversize():
         # the same kernels on the same inputs: bit-identical to engram_forward
         assert torch.equal(h_na, h_ref)
         assert torch.equal(g_na, g_ref)
-        # and within the oracle's bars on sampled rows (rows are independent)
+        # and within the oracle's bars on sampled rows (rows are independent):
+        # k/v against the oracle's, hidden end to end, and the gate on the
+        # k/v that engram_forward (bit-identical to this call) left in its
+        # workspace
         win, dead, _ = O.walk(tok, cu, hist, w.tmap, p.pad_cid)
         rows = np.unique(np.concatenate([rng.choice(T, size=min(T, 40), replace=False),
                                          np.flatnonzero(dead)[:4], [T - 1]]))
         idx = O.hash_windows(win[rows], dead[rows], p.mult, p.prime, p.offset)
         kv = O.project(O.gather_decode(idx, w.rows(0)), wkv)
-        new_h, g, dots = O.gate_residual(hidden[rows], kv, wqk, dead[rows], cfg.H, cfg.hc, 1e-6,
-                                         dot_scale)
+        _, got_kv, has = forward_rows(ws, T, S, cfg.H, cfg.hc, rows)
+        live = has & ~dead[rows]
+        assert_bf16_close(got_kv[live], kv[live], what=f"call {call} kv")
         got_h = down16(h_na).reshape(T, cfg.hc, cfg.H)[rows]
-        assert_bf16_close(got_h.reshape(-1, cfg.H), new_h.reshape(-1, cfg.H), what="hidden")
-        assert np.array_equal(got_h[dead[rows]], hidden[rows][dead[rows]])
         got_g = g_na.cpu().numpy().reshape(T, cfg.hc)[rows]
-        well = np.abs(dots) >= 1e-2
-        assert np.max(np.abs(got_g - g)[well]) <= 1e-3
-        assert np.all(got_g[dead[rows]] == 0)
+        check_gate_rows(got_h, got_g, hidden[rows], got_kv, kv, wqk, dead[rows], cfg.H, cfg.hc,
+                        dot_scale, what=f"call {call}")
     # a batch whose workspace exceeds the device array (64 MiB holds 1,055
     # tokens at H = 5,120, hc = 4) is rejected before any launch
     assert E.engram_forward_workspace(1055, cfg.H, cfg.hc) <= E.NOALLOC_WORKSPACE_BYTES
