@@ -12,9 +12,11 @@
  * Conventions for every entry point:
  *  - Array pointers are DEVICE pointers owned by the caller. The library never
  *    allocates or frees memory the caller sees, keeps no state between calls
- *    and never synchronises the host with the device.
+ *    (apart from engram_forward_noalloc's device array, see there) and never
+ *    synchronises the host with the device.
  *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
- *    at once. Calls are thread-safe.
+ *    at once. Calls are thread-safe (engram_forward_noalloc calls that overlap
+ *    on one GPU race on its array).
  *  - BF16 values travel as uint16_t bit patterns.
  *  - Shapes, pointers, alignment and parameter tables are checked on the host
  *    before anything is launched; a failed check returns ENGRAM_EINVAL and
